@@ -1,0 +1,154 @@
+/*
+ * seedmm.h -- C ABI of the SeedLM seed-decoding matrix products for AMD MI355X (gfx950).
+ *
+ * What the library computes.  A weight matrix W[M][K] is stored as blocks of 8
+ * consecutive weights along K (block b = m*(K/8) + k/8).  Each block holds a 16-bit
+ * LFSR seed, P (3 or 4) signed int4 coefficients and a 4-bit exponent code; each
+ * matrix holds one int32 exp_bias (model card "K2-Horizon-MoVA-36B-A4B - NanoSeedLM
+ * p4mx-q4v", section "This upload": NAME.seeds U16, NAME.coefs U16, NAME.codes U8,
+ * NAME.exp_bias I32).  The kernels regenerate each block inside the product and never
+ * write W back (NanoSeedLM README, "Highlights"; barnson.org post, "Never decompress"):
+ *
+ *     w_i = 2^(code + exp_bias - 15) * sum_{j<P} c_j * (s_{iP+j+1} - 32768),  i = 0..7
+ *
+ * where s_1, s_2, ... are the states after steps 1, 2, ... of a 16-bit Fibonacci
+ * register started at the seed (shift left, new bit = parity(state & 0xB400)), the
+ * basis is filled row-major, c_j = (q ^ 8) - 8 for nibble q (barnson.org post, "LFSR is
+ * free"), and the power of two multiplies (barnson.org post, "Attempt one").
+ *
+ * Stream layout of one matrix (all little-endian):
+ *   seeds  uint16[M*K/8]              one seed per block;
+ *   coefs  uint16[ceil(M*K/8*P/4)]    one nibble stream, P nibbles per block, nibble
+ *                                     n = b*P + j at word n>>2, bits 4*(n&3);
+ *   codes  uint8 [ceil(M*K/16)]       two 4-bit codes per byte, even block in the low nibble.
+ * Stacked experts ([E] matrices of equal shape) are the E single-matrix streams
+ * concatenated; this requires (M*K/8)*P % 4 == 0 and (M*K/8) % 2 == 0.  The weights
+ * are exact in fp32: |sum| <= 2^20 and the scale is a power of two.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller (e.g. PyTorch tensors).
+ *     The library allocates no memory and keeps no mutable global state; calls are
+ *     reentrant.  Scratch memory for seedmm_moe is passed in by the caller.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL = the
+ *     default stream).  Results are valid after the stream is synchronised.
+ *   - Arguments are validated before anything is launched; an error returns a negative
+ *     status and launches nothing.  SEEDMM_EHIP reports a failed kernel launch
+ *     (hipGetLastError); faults during execution surface at the next synchronisation.
+ *   - Limits: K % 8 == 0; P in {3, 4}; exp_bias in [-100, 100] (keeps every weight a
+ *     normal fp32); activation rows 16-byte aligned (x pointer 16-byte aligned, ldx a
+ *     multiple of 8 elements for bf16 and of 4 for fp32).  Seed streams that are 16-byte
+ *     aligned with K % 64 == 0 take the vector-load path; other layouts take a per-block
+ *     path with the same results.
+ */
+#ifndef SEEDMM_H
+#define SEEDMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SEEDMM_OK = 0,
+    SEEDMM_EINVAL = -1,     /* null pointer, bad size, bad P / dtype / exp_bias / ld   */
+    SEEDMM_EALIGN = -2,     /* activation or output pointer / leading dim misaligned  */
+    SEEDMM_EWORKSPACE = -3, /* workspace missing or smaller than seedmm_moe_workspace_bytes */
+    SEEDMM_EHIP = -4        /* the HIP runtime reported a launch failure              */
+};
+
+enum { SEEDMM_F32 = 0, SEEDMM_BF16 = 1 };
+
+/* One seed-coded matrix, or E stacked matrices of one shape (streams concatenated). */
+typedef struct seedmm_mat {
+    const uint16_t *seeds;    /* NAME.seeds                                     */
+    const uint16_t *coefs;    /* NAME.coefs (nibble stream)                     */
+    const uint8_t *codes;     /* NAME.codes (two codes per byte)                */
+    const int32_t *exp_bias;  /* NAME.exp_bias, int32[E] in device memory      */
+} seedmm_mat;
+
+/*
+ * seedmm_gemv -- y = W x for one fp32 activation vector (the decode matrix-vector
+ * product of the SeedLM pages: NanoSeedLM README "How it works").
+ *   seeds/coefs/codes: one [M][K] matrix;  exp_bias: its bias (by value);
+ *   x: fp32[K];  y: fp32[M] (overwritten).  Runs on the default stream.
+ *   Accumulates in fp32 with exact fp32 weights.
+ * Errors: SEEDMM_EINVAL (null pointer, M < 0, K < 0, K % 8 != 0, P not 3/4, exp_bias
+ * out of range), SEEDMM_EALIGN (x not 16-byte aligned), SEEDMM_EHIP.
+ */
+int seedmm_gemv(const uint16_t *seeds, const uint16_t *coefs, const uint8_t *codes,
+                int32_t exp_bias, const float *x, float *y, int M, int K, int P);
+
+/*
+ * seedmm_gemv_ex -- Y[n] = W X[n] for N activation rows.
+ *   x: row-major [N][ldx] of dtype x_dtype (SEEDMM_F32 or SEEDMM_BF16 raw bits);
+ *   y: fp32 row-major [N][ldy], overwritten (ldy >= M).
+ *   fp32 x: fp32 products and sums with exact weights.  bf16 x: the block weights are
+ *   rounded to bf16 (nearest even) and multiplied on the matrix cores with fp32
+ *   accumulation.
+ * Errors: as seedmm_gemv, plus SEEDMM_EINVAL for N < 0, ldx < K, ldy < M, bad dtype;
+ * SEEDMM_EALIGN for a misaligned x or ldx.
+ */
+int seedmm_gemv_ex(const uint16_t *seeds, const uint16_t *coefs, const uint8_t *codes,
+                   int32_t exp_bias, const void *x, int x_dtype, int ldx, float *y, int ldy,
+                   int M, int K, int P, int N, void *hip_stream);
+
+/*
+ * seedmm_reconstruct -- write W[M][K] row-major: fp32 (exact) or bf16 (round to nearest
+ * even of the exact fp32).  The reference point for bit-exact checks; the products
+ * above never materialise W.
+ * Errors: SEEDMM_EINVAL (null pointer, bad size, P, dtype or exp_bias), SEEDMM_EHIP.
+ */
+int seedmm_reconstruct(const uint16_t *seeds, const uint16_t *coefs, const uint8_t *codes,
+                       int32_t exp_bias, void *W, int w_dtype, int M, int K, int P,
+                       void *hip_stream);
+
+/*
+ * seedmm_moe_dispatch -- group the (token, slot) pairs of a routed batch by expert.
+ *   topk_ids: int32[T][top_k], each in [0, E) and distinct within a token.
+ *   counts: int32[E] (out) -- number of pairs routed to each expert;
+ *   lists:  int32[E][T] (out) -- expert e's pair indices p = t*top_k + slot, in
+ *           increasing order, in lists[e*T .. e*T + counts[e]).  Entries past counts[e]
+ *           are not written.
+ * Deterministic.  Ids outside [0, E) are counted nowhere (the caller validates ids).
+ * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k < 1, E < 1), SEEDMM_EHIP.
+ */
+int seedmm_moe_dispatch(const int32_t *topk_ids, int T, int top_k, int E, int32_t *counts,
+                        int32_t *lists, void *hip_stream);
+
+/* Bytes of scratch memory seedmm_moe needs for a batch of T tokens (0 on bad args). */
+size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
+
+/*
+ * seedmm_moe -- one routed mixture-of-experts layer of SwiGLU experts whose weights
+ * are seeds (K2-Horizon card "This upload": routed FFN experts are SeedLM P=4):
+ *     y[t] = sum_{s < top_k} topk_w[t][s] * down_e( silu(gate_e x[t]) * (up_e x[t]) ),
+ *     e = topk_ids[t][s],  silu(z) = z / (1 + exp(-z)).
+ *   x: bf16 [T][H] (raw bits), y: fp32 [T][H] (overwritten);
+ *   gate, up: E stacked [I][H] matrices; down: E stacked [H][I] matrices;
+ *   workspace: device scratch of at least seedmm_moe_workspace_bytes(T, top_k, E, H, I)
+ *   bytes, 256-byte aligned; its contents need not be initialised.
+ *   Expert products run on the matrix cores with bf16 weights and fp32 accumulation;
+ *   the SwiGLU output is rounded to bf16 before the down product; the slots of a token
+ *   are summed in slot order, so results are bit-reproducible.
+ * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], E < 1 or
+ * > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
+ * SEEDMM_EALIGN (x not 16-byte aligned or H % 8 != 0), SEEDMM_EWORKSPACE, SEEDMM_EHIP.
+ */
+int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+               const void *x, float *y, int E, int H, int I, int P,
+               seedmm_mat gate, seedmm_mat up, seedmm_mat down,
+               void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Static description of a status code. */
+const char *seedmm_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int seedmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEEDMM_H */

@@ -1,0 +1,53 @@
+"""Build the HIP library libseedmm.so in-tree for gfx950.
+
+    python -m pseudo_random_weight_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SO = os.path.join(HERE, "libseedmm.so")
+SOURCES = [os.path.join(CSRC, "seedmm.hip")]
+HEADERS = [os.path.join(CSRC, "seed_decode.hpp"), os.path.join(ROOT, "include", "seedmm.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    # no packed fp32 instructions in any device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = SO + ".tmp"
+    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libseedmm.so")
+    os.replace(tmp, SO)
+    return SO
+
+
+def asm(out: str = None) -> str:
+    """Device assembly of the library (for inspecting the generated gfx950 code)."""
+    out = out or os.path.join(ROOT, "_work", "seedmm.s")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-S",
+           "--cuda-device-only", *SOURCES, "-o", out]
+    subprocess.check_call(cmd)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,722 @@
+// seedmm.hip -- gfx950 kernels and the C ABI of the SeedLM seed-decoding products.
+//
+// Every kernel regenerates the weight blocks it needs from (seed, coefficients,
+// exponent code) in registers and consumes them at once; no kernel but
+// seedmm_reconstruct writes a weight to memory (NanoSeedLM README, "Highlights";
+// barnson.org post, "Never decompress").
+//
+// Work mapping shared by the product kernels.  A wave owns 16 rows of one matrix.
+// Lane l = r + 16 q (r = l % 16, q = l / 16) decodes blocks of row r in runs of 8
+// consecutive blocks ("segments"), so one lane's 8 seeds, 8 coefficient words and 8
+// codes arrive in three vector loads.  Segments are dealt round-robin to the 4 lane
+// quarters and to the waves that split K.  At each step a lane holds one block = 8
+// consecutive k of its row, which is exactly the A operand of one
+// v_mfma_f32_16x16x32_bf16 lane (16 rows x 32 k per wave); the matching B lane holds the
+// same 8 k of one token.  The k order inside the MFMA is a permutation of the true k
+// order, applied identically to A and B.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/seedmm.h"
+#include "seed_decode.hpp"
+
+namespace seedmm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum { MODE_GEMM = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
+
+// ----------------------------------------------------------------------------------
+// Stream access for a run of 8 blocks starting at block b0 of one matrix.
+// VEC: b0 % 8 == 0 and the stream bases are 16-byte aligned -> three vector loads.
+// Otherwise each block is read on its own (any K % 8 == 0, any alignment).
+// ----------------------------------------------------------------------------------
+template <int P, bool VEC>
+struct Seg {
+    uint32_t sd[4];                   // VEC: seeds, two per word
+    uint32_t cf[P == 4 ? 4 : 3];      // VEC: 8 blocks of P nibbles
+    uint32_t cd;                      // VEC: 8 codes
+    uint32_t s1[8], c1[8], d1[8];     // per-block path
+
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ seeds,
+                                         const uint16_t* __restrict__ coefs,
+                                         const uint8_t* __restrict__ codes, int64_t b0,
+                                         int nvalid) {
+        if constexpr (VEC) {
+            const uint4 s = *reinterpret_cast<const uint4*>(seeds + b0);
+            sd[0] = s.x; sd[1] = s.y; sd[2] = s.z; sd[3] = s.w;
+            if constexpr (P == 4) {
+                const uint4 c = *reinterpret_cast<const uint4*>(coefs + b0);
+                cf[0] = c.x; cf[1] = c.y; cf[2] = c.z; cf[3] = c.w;
+            } else {
+                const uint32_t* c = reinterpret_cast<const uint32_t*>(coefs) + (b0 * 3) / 8;
+                cf[0] = c[0]; cf[1] = c[1]; cf[2] = c[2];
+            }
+            cd = *reinterpret_cast<const uint32_t*>(codes + b0 / 2);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                s1[s] = 0; c1[s] = 0; d1[s] = 0;
+                if (s < nvalid) {
+                    const int64_t b = b0 + s;
+                    s1[s] = seeds[b];
+                    if constexpr (P == 4) {
+                        c1[s] = coefs[b];
+                    } else {
+                        const int64_t n = b * 3;
+                        const int sh = 4 * (int)(n & 3);
+                        uint32_t v = (uint32_t)coefs[n >> 2] >> sh;
+                        if (sh > 4) v |= (uint32_t)coefs[(n >> 2) + 1] << (16 - sh);
+                        c1[s] = v;
+                    }
+                    d1[s] = ((uint32_t)codes[b >> 1] >> (4 * (int)(b & 1))) & 0xFu;
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ uint32_t seed(int s) const {
+        if constexpr (VEC) return __builtin_amdgcn_ubfe(sd[s >> 1], 16 * (s & 1), 16);
+        else return s1[s];
+    }
+    __device__ __forceinline__ uint32_t coef(int s) const {
+        if constexpr (VEC) {
+            if constexpr (P == 4) {
+                return __builtin_amdgcn_ubfe(cf[s >> 1], 16 * (s & 1), 16);
+            } else {
+                const int bit = 12 * s, w = bit >> 5, sh = bit & 31;
+                return sh <= 20 ? (cf[w] >> sh)
+                                : __builtin_amdgcn_alignbit(cf[w + 1], cf[w], sh);
+            }
+        } else {
+            return c1[s];
+        }
+    }
+    __device__ __forceinline__ uint32_t code(int s) const {
+        if constexpr (VEC) return __builtin_amdgcn_ubfe(cd, 4 * s, 4);
+        else return d1[s];
+    }
+};
+
+// Base pointers of matrix `e` of E stacked [M][K] matrices.
+struct Mat {
+    const uint16_t* seeds;
+    const uint16_t* coefs;
+    const uint8_t* codes;
+    int exp_bias;
+};
+
+__device__ __forceinline__ Mat mat_of(const seedmm_mat& m, int e, int64_t nblk, int P,
+                                      int eb_scalar, bool eb_from_ptr) {
+    Mat r;
+    r.seeds = m.seeds + (int64_t)e * nblk;
+    r.coefs = m.coefs + (int64_t)e * (nblk * P / 4);
+    r.codes = m.codes + (int64_t)e * (nblk / 2);
+    r.exp_bias = eb_from_ptr ? m.exp_bias[e] : eb_scalar;
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16(const float w[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)w[i];
+    return v;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
+    return v;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// ----------------------------------------------------------------------------------
+// seedmm_reconstruct: one thread per block, writes the block's 8 weights.
+// ----------------------------------------------------------------------------------
+template <int P, bool BF16>
+__global__ __launch_bounds__(256) void k_reconstruct(const uint16_t* __restrict__ seeds,
+                                                     const uint16_t* __restrict__ coefs,
+                                                     const uint8_t* __restrict__ codes,
+                                                     int exp_bias, void* __restrict__ W,
+                                                     int K, int64_t nblk) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    Seg<P, false> sg;
+    sg.load(seeds, coefs, codes, b, 1);
+    const Window win = lfsr_window(sg.seed(0));
+    float w[8];
+    decode_block<P>(win, sg.coef(0), sg.code(0), exp_bias, w);
+    const int nbpr = K / 8;
+    const int64_t m = b / nbpr, kb = b % nbpr;
+    if constexpr (BF16) {
+        bf16x8 v = pack_bf16(w);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(W) + m * K + 8 * kb) =
+            __builtin_bit_cast(uint4, v);
+    } else {
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(W) + m * K + 8 * kb);
+        o[0] = make_float4(w[0], w[1], w[2], w[3]);
+        o[1] = make_float4(w[4], w[5], w[6], w[7]);
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// fp32 activations: products on the vector ALUs with exact fp32 weights.
+// 4 waves split K; NTOK activation rows per pass.
+// ----------------------------------------------------------------------------------
+template <int P, bool VEC, int NTOK>
+__global__ __launch_bounds__(256) void k_gemv_f32(const uint16_t* __restrict__ seeds,
+                                                  const uint16_t* __restrict__ coefs,
+                                                  const uint8_t* __restrict__ codes,
+                                                  int exp_bias, const float* __restrict__ x,
+                                                  int ldx, float* __restrict__ y, int ldy,
+                                                  int M, int K, int N) {
+    __shared__ float red[4][NTOK][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int row = blockIdx.x * 16 + r;
+    const bool rv = row < M;
+    const int nbpr = K / 8;
+    const int nseg = (nbpr + 7) / 8;
+    const int n_it = (nseg + 15) / 16;
+    const int n0 = blockIdx.y * NTOK;
+    const int64_t rowb = (int64_t)(rv ? row : 0) * nbpr;
+
+    float acc[NTOK];
+#pragma unroll
+    for (int n = 0; n < NTOK; ++n) acc[n] = 0.0f;
+
+    for (int it = 0; it < n_it; ++it) {
+        const int g = it * 16 + wave * 4 + q;
+        if (!(g < nseg && rv)) continue;
+        const int nvalid = min(8, nbpr - g * 8);
+        Seg<P, VEC> sg;
+        sg.load(seeds, coefs, codes, rowb + g * 8, nvalid);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (!VEC && s >= nvalid) break;
+            const int kb = g * 8 + s;
+            const Window win = lfsr_window(sg.seed(s));
+            int f[8];
+            block_sums<P>(win, sg.coef(s), f);
+            const float sc = block_scale(sg.code(s), exp_bias);
+#pragma unroll
+            for (int n = 0; n < NTOK; ++n) {
+                if (n0 + n < N) {
+                    const float4* xp =
+                        reinterpret_cast<const float4*>(x + (int64_t)(n0 + n) * ldx + 8 * kb);
+                    const float4 xa = xp[0], xb = xp[1];
+                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                    float blk = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        blk = __builtin_fmaf(xv[i], __int_as_float(f[i]) - kMagic, blk);
+                    acc[n] = __builtin_fmaf(blk, sc, acc[n]);
+                }
+            }
+        }
+    }
+    // reduce the four lane quarters of each row, then the four waves
+#pragma unroll
+    for (int n = 0; n < NTOK; ++n) {
+        float v = acc[n];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (q == 0) red[wave][n][r] = v;
+    }
+    __syncthreads();
+    if (wave == 0 && q == 0 && rv) {
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+            if (n0 + n < N)
+                y[(int64_t)(n0 + n) * ldy + row] =
+                    ((red[0][n][r] + red[1][n][r]) + red[2][n][r]) + red[3][n][r];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// bf16 activations: weights regenerated per lane, rounded to bf16, multiplied on the
+// matrix cores (16x16x32 bf16 -> fp32).
+//   MODE_GEMM   : y[n][m] = sum_k W[m][k] x[n][k]                       (one matrix)
+//   MODE_GATEUP : h[p][m] = bf16( silu(G_e x_t)[m] * (U_e x_t)[m] ),  t = p / top_k
+//   MODE_DOWN   : o[p][m] = w[p] * (D_e h_p)[m]
+// Grid: x = row tiles (16 * ROWT rows), y = active experts (expert y = the y-th expert
+// with a nonzero count).  KSPLIT waves split K (then ROWT = 1) or ROWT = 4 waves own
+// different rows (KSPLIT = 1).  Tokens are processed in passes of NT*16.
+// ----------------------------------------------------------------------------------
+struct MfmaArgs {
+    seedmm_mat A;           // gate (GATEUP) or the matrix
+    seedmm_mat A2;          // up (GATEUP)
+    int exp_bias;           // GEMM: scalar exp_bias
+    int M, K, P_unused;
+    const uint16_t* x;      // GEMM/GATEUP: activations bf16 [.][ldx]; DOWN: h [.][ldx]
+    int ldx;
+    int N;                  // GEMM: number of rows of x
+    const int32_t* counts;  // experts: int32[E]
+    const int32_t* lists;   // experts: int32[E][T]
+    int E, T, top_k;
+    const float* topk_w;    // DOWN
+    float* y;               // GEMM: fp32 [N][ldy]; DOWN: fp32 [T*top_k][ldy]
+    uint16_t* h;            // GATEUP: bf16 [T*top_k][ldy]
+    int ldy;
+};
+
+template <int P, bool VEC, int NT, int MODE, int KSPLIT>
+__global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
+    constexpr int ROWT = 4 / KSPLIT;
+    constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
+    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][KSPLIT > 1 ? NT * NMAT : 1][64];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int ks = wave % KSPLIT, rt = wave / KSPLIT;
+
+    // ---- which expert this workgroup serves --------------------------------------
+    int e = 0, n_e = a.N;
+    const int32_t* list = nullptr;
+    if constexpr (MODE != MODE_GEMM) {
+        const int target = blockIdx.y;
+        int found = -1, cum = 0;
+        for (int base = 0; base < a.E && found < 0; base += 64) {
+            const int idx = base + lane;
+            const bool act = idx < a.E && a.counts[idx] > 0;
+            const uint64_t bal = __ballot(act);
+            const int c = __popcll(bal);
+            if (target < cum + c) {
+                const int k = target - cum;
+                const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+                const bool mine = act && __popcll(below) == k;
+                found = base + __ffsll((long long)__ballot(mine)) - 1;
+            }
+            cum += c;
+        }
+        if (found < 0) return;   // uniform across the workgroup
+        e = found;
+        n_e = a.counts[e];
+        list = a.lists + (int64_t)e * a.T;
+    }
+
+    const int M = a.M, K = a.K;
+    const int nbpr = K / 8;
+    const int64_t nblk = (int64_t)M * nbpr;
+    const Mat W1 = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
+    Mat W2 = W1;
+    if constexpr (MODE == MODE_GATEUP) W2 = mat_of(a.A2, e, nblk, P, 0, true);
+
+    const int m0 = (blockIdx.x * ROWT + rt) * 16;
+    const int row = m0 + r;
+    const bool rv = row < M;
+    const int64_t rowb = (int64_t)(rv ? row : 0) * nbpr;
+    const int nseg = (nbpr + 7) / 8;
+    constexpr int GSTRIDE = KSPLIT * 4;
+    const int n_it = (nseg + GSTRIDE - 1) / GSTRIDE;
+
+    for (int pass = 0; pass < n_e; pass += NT * 16) {
+        const int ntiles = min(NT, (n_e - pass + 15) / 16);
+        // B rows of this lane: token column r of every tile
+        const uint16_t* brow[NT];
+        bool bv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int i = pass + 16 * t + r;
+            bv[t] = i < n_e;
+            int64_t src = 0;
+            if (bv[t]) {
+                if constexpr (MODE == MODE_GEMM) src = i;
+                else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
+                else src = list[i];
+            }
+            brow[t] = a.x + src * a.ldx;
+        }
+
+        f32x4 acc[NT], acc2[NMAT == 2 ? NT : 1];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < (NMAT == 2 ? NT : 1); ++t) acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int it = 0; it < n_it; ++it) {
+            const int g = it * GSTRIDE + ks * 4 + q;
+            const bool gv = g < nseg;
+            const int nvalid = gv ? min(8, nbpr - g * 8) : 0;
+            Seg<P, VEC> s1, s2;
+            if (gv && rv) {
+                s1.load(W1.seeds, W1.coefs, W1.codes, rowb + g * 8, nvalid);
+                if constexpr (NMAT == 2) s2.load(W2.seeds, W2.coefs, W2.codes, rowb + g * 8, nvalid);
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int kb = g * 8 + s;
+                const bool kv = s < nvalid;
+                bf16x8 A = zero_bf16x8(), A2 = zero_bf16x8();
+                if (kv && rv) {
+                    float w[8];
+                    decode_block<P>(lfsr_window(s1.seed(s)), s1.coef(s), s1.code(s),
+                                    W1.exp_bias, w);
+                    A = pack_bf16(w);
+                    if constexpr (NMAT == 2) {
+                        decode_block<P>(lfsr_window(s2.seed(s)), s2.coef(s), s2.code(s),
+                                        W2.exp_bias, w);
+                        A2 = pack_bf16(w);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t < ntiles) {
+                        bf16x8 B = zero_bf16x8();
+                        if (kv && bv[t]) B = load_bf16x8(brow[t] + 8 * kb);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
+                        if constexpr (NMAT == 2)
+                            acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc2[t], 0, 0, 0);
+                    }
+                }
+            }
+        }
+
+        // ---- reduce the K split and write -------------------------------------------
+        if constexpr (KSPLIT > 1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t < ntiles) {
+                    red[ks][t][lane] = acc[t];
+                    if constexpr (NMAT == 2) red[ks][NT + t][lane] = acc2[t];
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t >= ntiles) continue;
+            if (KSPLIT > 1 && (t % KSPLIT) != ks) continue;
+            f32x4 v = acc[t], v2 = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (NMAT == 2) v2 = acc2[t];
+            if constexpr (KSPLIT > 1) {
+                v = red[0][t][lane];
+#pragma unroll
+                for (int w = 1; w < KSPLIT; ++w) v += red[w][t][lane];
+                if constexpr (NMAT == 2) {
+                    v2 = red[0][NT + t][lane];
+#pragma unroll
+                    for (int w = 1; w < KSPLIT; ++w) v2 += red[w][NT + t][lane];
+                }
+            }
+            const int i = pass + 16 * t + r;     // D column = token slot
+            if (i >= n_e) continue;
+            int64_t dst;
+            float scale = 1.0f;
+            if constexpr (MODE == MODE_GEMM) {
+                dst = i;
+            } else {
+                dst = list[i];
+                if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + 4 * q + j;   // D row
+                if (m >= M) continue;
+                if constexpr (MODE == MODE_GATEUP) {
+                    const float gt = v[j], up = v2[j];
+                    const float hv = gt / (1.0f + expf(-gt)) * up;
+                    const __bf16 hb = (__bf16)hv;
+                    a.h[dst * a.ldy + m] = __builtin_bit_cast(uint16_t, hb);
+                } else {
+                    a.y[dst * a.ldy + m] = scale * v[j];
+                }
+            }
+        }
+        if constexpr (KSPLIT > 1) __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// MoE dispatch: workgroup e compacts the pairs routed to expert e, in pair order.
+// ----------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dispatch(const int32_t* __restrict__ ids, int total,
+                                                  int T, int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ lists) {
+    __shared__ int wsum[4];
+    const int e = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int base = 0;
+    int32_t* out = lists + (int64_t)e * T;
+    for (int p0 = 0; p0 < total; p0 += 256) {
+        const int p = p0 + threadIdx.x;
+        const bool hit = p < total && ids[p] == e;
+        const uint64_t bal = __ballot(hit);
+        const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+        if (lane == 0) wsum[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        const int slot = base + before + __popcll(below);
+        if (hit && slot < T) out[slot] = p;   // ids repeated within a token: dropped
+        base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) counts[e] = base < T ? base : T;
+}
+
+// y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, int top_k,
+                                                 float* __restrict__ y, int H, int T) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
+    const int h4 = H / 4;
+    if (idx >= (int64_t)T * h4) return;
+    const int64_t t = idx / h4, c = idx % h4;
+    const float4* src = reinterpret_cast<const float4*>(o) + (t * top_k) * h4 + c;
+    float4 s = src[0];
+    for (int k = 1; k < top_k; ++k) {
+        const float4 v = src[(int64_t)k * h4];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    reinterpret_cast<float4*>(y)[idx] = s;
+}
+
+}  // namespace seedmm
+
+// ==================================================================================
+// Host side: validation, path selection, launches.
+// ==================================================================================
+using namespace seedmm;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_shape(int M, int K, int P) {
+    return M >= 0 && K >= 0 && K % 8 == 0 && (P == 3 || P == 4);
+}
+
+bool valid_bias(int32_t eb) { return eb >= -100 && eb <= 100; }
+
+// Vector-load path: every row starts a whole segment and every base is 16-byte aligned.
+bool use_vec(const void* seeds, const void* coefs, const void* codes, int K) {
+    return K % 64 == 0 && aligned16(seeds) && aligned16(coefs) && aligned16(codes);
+}
+
+int launch_status() {
+    return hipGetLastError() == hipSuccess ? SEEDMM_OK : SEEDMM_EHIP;
+}
+
+template <int P, bool VEC, int NTOK>
+void launch_gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int eb,
+                     const float* x, int ldx, float* y, int ldy, int M, int K, int N,
+                     hipStream_t st) {
+    dim3 grid((M + 15) / 16, (N + NTOK - 1) / NTOK);
+    hipLaunchKernelGGL((k_gemv_f32<P, VEC, NTOK>), grid, dim3(256), 0, st, s, c, d, eb, x, ldx,
+                       y, ldy, M, K, N);
+}
+
+template <int P>
+void gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int eb, const float* x,
+              int ldx, float* y, int ldy, int M, int K, int N, hipStream_t st) {
+    const bool vec = use_vec(s, c, d, K);
+    if (N <= 1) {
+        if (vec) launch_gemv_f32<P, true, 1>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
+        else launch_gemv_f32<P, false, 1>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
+    } else {
+        if (vec) launch_gemv_f32<P, true, 4>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
+        else launch_gemv_f32<P, false, 4>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
+    }
+}
+
+// Decode shape: 4 waves split K, up to 64 tokens per pass.  Prefill shape: 4 waves on
+// 4 row tiles, up to 256 tokens per pass.
+template <int P, bool VEC, int MODE>
+void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
+    if (prefill) {
+        dim3 grid((a.M + 63) / 64, gridy);
+        hipLaunchKernelGGL((k_mfma<P, VEC, 16, MODE, 1>), grid, dim3(256), 0, st, a);
+    } else {
+        dim3 grid((a.M + 15) / 16, gridy);
+        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, 4>), grid, dim3(256), 0, st, a);
+    }
+}
+
+template <int MODE>
+void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
+    if (P == 4) {
+        if (vec) launch_mfma<4, true, MODE>(a, prefill, gridy, st);
+        else launch_mfma<4, false, MODE>(a, prefill, gridy, st);
+    } else {
+        if (vec) launch_mfma<3, true, MODE>(a, prefill, gridy, st);
+        else launch_mfma<3, false, MODE>(a, prefill, gridy, st);
+    }
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct MoeLayout {
+    size_t counts, lists, h, o, total;
+};
+
+bool moe_layout(int T, int top_k, int E, int H, int I, MoeLayout* L) {
+    if (T < 0 || top_k < 1 || E < 1 || H < 0 || I < 0) return false;
+    const size_t pairs = (size_t)T * top_k;
+    L->counts = 0;
+    L->lists = L->counts + align_up(sizeof(int32_t) * (size_t)E);
+    L->h = L->lists + align_up(sizeof(int32_t) * (size_t)E * (size_t)T);
+    L->o = L->h + align_up(sizeof(uint16_t) * pairs * (size_t)I);
+    L->total = L->o + align_up(sizeof(float) * pairs * (size_t)H);
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int seedmm_version(void) { return 100; }
+
+const char* seedmm_strerror(int status) {
+    switch (status) {
+        case SEEDMM_OK: return "ok";
+        case SEEDMM_EINVAL: return "invalid argument";
+        case SEEDMM_EALIGN: return "misaligned pointer or leading dimension";
+        case SEEDMM_EWORKSPACE: return "workspace missing or too small";
+        case SEEDMM_EHIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+int seedmm_gemv_ex(const uint16_t* seeds, const uint16_t* coefs, const uint8_t* codes,
+                   int32_t exp_bias, const void* x, int x_dtype, int ldx, float* y, int ldy,
+                   int M, int K, int P, int N, void* hip_stream) {
+    if (!valid_shape(M, K, P) || !valid_bias(exp_bias) || N < 0 || ldx < K || ldy < M)
+        return SEEDMM_EINVAL;
+    if (x_dtype != SEEDMM_F32 && x_dtype != SEEDMM_BF16) return SEEDMM_EINVAL;
+    if (M == 0 || N == 0) return SEEDMM_OK;
+    if (!seeds || !coefs || !codes || !x || !y) return SEEDMM_EINVAL;
+    if (!aligned16(x)) return SEEDMM_EALIGN;
+    hipStream_t st = (hipStream_t)hip_stream;
+    if (K == 0) {   // empty product: y = 0
+        for (int n = 0; n < N; ++n)
+            if (hipMemsetAsync(y + (int64_t)n * ldy, 0, sizeof(float) * (size_t)M, st) != hipSuccess)
+                return SEEDMM_EHIP;
+        return SEEDMM_OK;
+    }
+    if (x_dtype == SEEDMM_F32) {
+        if (ldx % 4 != 0) return SEEDMM_EALIGN;
+        if (P == 4) gemv_f32<4>(seeds, coefs, codes, exp_bias, (const float*)x, ldx, y, ldy, M, K, N, st);
+        else gemv_f32<3>(seeds, coefs, codes, exp_bias, (const float*)x, ldx, y, ldy, M, K, N, st);
+        return launch_status();
+    }
+    if (ldx % 8 != 0) return SEEDMM_EALIGN;
+    MfmaArgs a = {};
+    a.A.seeds = seeds; a.A.coefs = coefs; a.A.codes = codes; a.A.exp_bias = nullptr;
+    a.exp_bias = exp_bias;
+    a.M = M; a.K = K;
+    a.x = (const uint16_t*)x; a.ldx = ldx; a.N = N;
+    a.y = y; a.ldy = ldy;
+    const bool vec = use_vec(seeds, coefs, codes, K);
+    mfma_dispatch<MODE_GEMM>(P, vec, a, N > 64, 1, st);
+    return launch_status();
+}
+
+int seedmm_gemv(const uint16_t* seeds, const uint16_t* coefs, const uint8_t* codes,
+                int32_t exp_bias, const float* x, float* y, int M, int K, int P) {
+    return seedmm_gemv_ex(seeds, coefs, codes, exp_bias, x, SEEDMM_F32, K < 4 ? 4 : K, y,
+                          M, M, K, P, 1, nullptr);
+}
+
+int seedmm_reconstruct(const uint16_t* seeds, const uint16_t* coefs, const uint8_t* codes,
+                       int32_t exp_bias, void* W, int w_dtype, int M, int K, int P,
+                       void* hip_stream) {
+    if (!valid_shape(M, K, P) || !valid_bias(exp_bias)) return SEEDMM_EINVAL;
+    if (w_dtype != SEEDMM_F32 && w_dtype != SEEDMM_BF16) return SEEDMM_EINVAL;
+    const int64_t nblk = (int64_t)M * (K / 8);
+    if (nblk == 0) return SEEDMM_OK;
+    if (!seeds || !coefs || !codes || !W) return SEEDMM_EINVAL;
+    if (!aligned16(W)) return SEEDMM_EALIGN;
+    hipStream_t st = (hipStream_t)hip_stream;
+    dim3 grid((unsigned)((nblk + 255) / 256));
+    if (P == 4) {
+        if (w_dtype == SEEDMM_BF16)
+            hipLaunchKernelGGL((k_reconstruct<4, true>), grid, dim3(256), 0, st, seeds, coefs, codes, exp_bias, W, K, nblk);
+        else
+            hipLaunchKernelGGL((k_reconstruct<4, false>), grid, dim3(256), 0, st, seeds, coefs, codes, exp_bias, W, K, nblk);
+    } else {
+        if (w_dtype == SEEDMM_BF16)
+            hipLaunchKernelGGL((k_reconstruct<3, true>), grid, dim3(256), 0, st, seeds, coefs, codes, exp_bias, W, K, nblk);
+        else
+            hipLaunchKernelGGL((k_reconstruct<3, false>), grid, dim3(256), 0, st, seeds, coefs, codes, exp_bias, W, K, nblk);
+    }
+    return launch_status();
+}
+
+int seedmm_moe_dispatch(const int32_t* topk_ids, int T, int top_k, int E, int32_t* counts,
+                        int32_t* lists, void* hip_stream) {
+    if (T < 0 || top_k < 1 || E < 1) return SEEDMM_EINVAL;
+    if (!counts || !lists || (T > 0 && !topk_ids)) return SEEDMM_EINVAL;
+    hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, (hipStream_t)hip_stream, topk_ids,
+                       T * top_k, T, counts, lists);
+    return launch_status();
+}
+
+size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I) {
+    MoeLayout L;
+    if (!moe_layout(T, top_k, E, H, I, &L)) return 0;
+    return L.total;
+}
+
+int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
+               float* y, int E, int H, int I, int P, seedmm_mat gate, seedmm_mat up,
+               seedmm_mat down, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (T < 0 || E < 1 || E > 4096 || top_k < 1 || top_k > E || top_k > 64) return SEEDMM_EINVAL;
+    if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0 || (P != 3 && P != 4)) return SEEDMM_EINVAL;
+    const int64_t nblk = (int64_t)I * (H / 8);   // blocks of one gate/up/down matrix
+    if ((nblk * P) % 4 != 0 || nblk % 2 != 0) return SEEDMM_EINVAL;
+    if (T == 0) return SEEDMM_OK;
+    const seedmm_mat* mats[3] = {&gate, &up, &down};
+    for (const seedmm_mat* m : mats)
+        if (!m->seeds || !m->coefs || !m->codes || !m->exp_bias) return SEEDMM_EINVAL;
+    if (!topk_ids || !topk_w || !x || !y) return SEEDMM_EINVAL;
+    if (!aligned16(x) || !aligned16(y)) return SEEDMM_EALIGN;
+    MoeLayout L;
+    moe_layout(T, top_k, E, H, I, &L);
+    if (!workspace || workspace_bytes < L.total) return SEEDMM_EWORKSPACE;
+    if (!aligned16(workspace)) return SEEDMM_EALIGN;
+    hipStream_t st = (hipStream_t)hip_stream;
+    char* ws = (char*)workspace;
+    int32_t* counts = (int32_t*)(ws + L.counts);
+    int32_t* lists = (int32_t*)(ws + L.lists);
+    uint16_t* hbuf = (uint16_t*)(ws + L.h);
+    float* obuf = (float*)(ws + L.o);
+
+    hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T, counts, lists);
+
+    const int pairs = T * top_k;
+    const int gridy = pairs < E ? pairs : E;          // at most this many active experts
+    const bool prefill = (int64_t)pairs >= 64LL * E;  // >= 64 tokens per expert on average
+    bool vec = true;
+    for (const seedmm_mat* m : mats) vec = vec && use_vec(m->seeds, m->coefs, m->codes, 64);
+    vec = vec && H % 64 == 0 && I % 64 == 0 && (nblk % 8 == 0);
+
+    MfmaArgs a = {};
+    a.A = gate; a.A2 = up;
+    a.M = I; a.K = H;
+    a.x = (const uint16_t*)x; a.ldx = H;
+    a.counts = counts; a.lists = lists; a.E = E; a.T = T; a.top_k = top_k;
+    a.h = hbuf; a.ldy = I;
+    mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
+
+    MfmaArgs b = {};
+    b.A = down;
+    b.M = H; b.K = I;
+    b.x = hbuf; b.ldx = I;
+    b.counts = counts; b.lists = lists; b.E = E; b.T = T; b.top_k = top_k;
+    b.topk_w = topk_w; b.y = obuf; b.ldy = H;
+    mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
+
+    const int64_t n4 = (int64_t)T * (H / 4);
+    if (H % 4 != 0) return SEEDMM_EINVAL;
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, obuf,
+                       top_k, y, H, T);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+"""Thin Python binding of the seedmm C ABI (include/seedmm.h).
+
+Argument marshalling only: tensors are passed to the HIP library as device pointers
+plus sizes, on torch's current HIP stream.  Every step of the computation runs in
+the library's kernels; there is no Python or CPU fallback, and a missing library
+raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libseedmm.so")
+
+OK, EINVAL, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+
+
+class SeedmmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_lib.seedmm_strerror(status).decode()} (status {status})")
+        self.status = status
+
+
+class SeedMat(ctypes.Structure):
+    _fields_ = [("seeds", ctypes.c_void_p), ("coefs", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("exp_bias", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m pseudo_random_weight_amd.build` "
+            "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32 = ctypes.c_void_p, ctypes.c_int
+    L.seedmm_gemv.argtypes = [p, p, p, ctypes.c_int32, p, p, i32, i32, i32]
+    L.seedmm_gemv_ex.argtypes = [p, p, p, ctypes.c_int32, p, i32, i32, p, i32, i32, i32, i32, i32, p]
+    L.seedmm_reconstruct.argtypes = [p, p, p, ctypes.c_int32, p, i32, i32, i32, i32, p]
+    L.seedmm_moe_dispatch.argtypes = [p, i32, i32, i32, p, p, p]
+    L.seedmm_moe_workspace_bytes.restype = ctypes.c_size_t
+    L.seedmm_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.seedmm_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, SeedMat, SeedMat, SeedMat,
+                             p, ctypes.c_size_t, p]
+    L.seedmm_strerror.restype = ctypes.c_char_p
+    L.seedmm_strerror.argtypes = [i32]
+    L.seedmm_version.restype = i32
+    for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
+                 "seedmm_moe"):
+        getattr(L, name).restype = i32
+    return L
+
+
+_lib = _load()
+
+EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
+           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_strerror", "seedmm_version")
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise SeedmmError(status, what)
+
+
+def _dev(t, dtype, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _mat(m: dict):
+    _dev(m["seeds"], torch.uint16, "seeds")
+    _dev(m["coefs"], torch.uint16, "coefs")
+    _dev(m["codes"], torch.uint8, "codes")
+    return m
+
+
+def gemv(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor = None):
+    """y = W x for fp32 x[K] (seedmm_gemv, default stream)."""
+    _mat(mat)
+    _dev(x, torch.float32, "x")
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
+    _check(_lib.seedmm_gemv(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
+                            _ptr(x), _ptr(y), M, K, P), "seedmm_gemv")
+    return y
+
+
+def gemv_ex(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor = None,
+            stream=None):
+    """Y[n] = W X[n] for X fp32 or bf16 [N][K] (seedmm_gemv_ex)."""
+    _mat(mat)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _dev(x, x.dtype, "x")
+    N = x.shape[0] if x.dim() == 2 else 1
+    ldx = x.shape[-1]
+    if y is None:
+        y = torch.empty((N, M), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
+    _check(_lib.seedmm_gemv_ex(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
+                               _ptr(x), F32 if x.dtype == torch.float32 else BF16, ldx, _ptr(y),
+                               y.shape[-1], M, K, P, N, _stream(stream)), "seedmm_gemv_ex")
+    return y
+
+
+def reconstruct(mat: dict, M: int, K: int, P: int, dtype=torch.float32, out=None, stream=None):
+    """W[M][K] in fp32 (exact) or bf16 (seedmm_reconstruct)."""
+    _mat(mat)
+    dev = mat["seeds"].device
+    if out is None:
+        out = torch.empty((M, K), dtype=dtype, device=dev)
+    _dev(out, dtype, "W")
+    eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
+    _check(_lib.seedmm_reconstruct(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
+                                   _ptr(out), F32 if dtype == torch.float32 else BF16, M, K, P,
+                                   _stream(stream)), "seedmm_reconstruct")
+    return out
+
+
+def moe_dispatch(topk_ids: torch.Tensor, E: int, stream=None):
+    """(counts int32[E], lists int32[E][T]) for topk_ids int32 [T][top_k]."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    counts = torch.empty(E, dtype=torch.int32, device=topk_ids.device)
+    lists = torch.full((E, max(T, 1)), -1, dtype=torch.int32, device=topk_ids.device)
+    _check(_lib.seedmm_moe_dispatch(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(lists),
+                                    _stream(stream)), "seedmm_moe_dispatch")
+    return counts, lists
+
+
+def moe_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int) -> int:
+    return int(_lib.seedmm_moe_workspace_bytes(T, top_k, E, H, I))
+
+
+def _seedmat(m: dict) -> SeedMat:
+    _mat(m)
+    _dev(m["exp_bias"], torch.int32, "exp_bias")
+    return SeedMat(m["seeds"].data_ptr(), m["coefs"].data_ptr(), m["codes"].data_ptr(),
+                   m["exp_bias"].data_ptr())
+
+
+def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None, stream=None):
+    """Routed SwiGLU MoE layer (seedmm_moe); x bf16 [T][H] -> y fp32 [T][H]."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float32, "topk_w")
+    _dev(x, torch.bfloat16, "x")
+    T, k = topk_ids.shape
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    need = moe_workspace_bytes(T, k, E, H, I)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(_lib.seedmm_moe(_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I, P,
+                           _seedmat(gate), _seedmat(up), _seedmat(down), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "seedmm_moe")
+    return y

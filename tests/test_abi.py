@@ -1,0 +1,118 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol, and
+rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seedmm.h")
+SO = os.path.join(ROOT, "pseudo_random_weight_amd", "libseedmm.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(seedmm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(SO):
+        pytest.fail("libseedmm.so is not built (python -m pseudo_random_weight_amd.build)")
+    from pseudo_random_weight_amd import seedmm
+    return seedmm.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    from pseudo_random_weight_amd import seedmm
+    assert set(seedmm.EXPORTS) == set(names)
+
+
+def test_version_and_strerror(lib):
+    assert lib.seedmm_version() >= 100
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.seedmm_strerror(st), bytes)
+
+
+FAKE = 0x100000   # 16-byte aligned address that is never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("M,K,P,eb,expect", [
+    (16, 12, 4, 0, -1),      # K % 8
+    (16, 16, 5, 0, -1),      # P
+    (16, 16, 2, 0, -1),
+    (-1, 16, 4, 0, -1),      # M < 0
+    (16, 16, 4, 101, -1),    # exp_bias out of range
+    (16, 16, 4, -101, -1),
+])
+def test_gemv_rejects_bad_shapes(lib, M, K, P, eb, expect):
+    assert lib.seedmm_gemv(FAKE, FAKE, FAKE, eb, FAKE, FAKE, M, K, P) == expect
+
+
+def test_gemv_rejects_null_and_misaligned(lib):
+    assert lib.seedmm_gemv(None, FAKE, FAKE, 0, FAKE, FAKE, 16, 16, 4) == -1
+    assert lib.seedmm_gemv(FAKE, FAKE, FAKE, 0, None, FAKE, 16, 16, 4) == -1
+    assert lib.seedmm_gemv(FAKE, FAKE, FAKE, 0, FAKE + 4, FAKE, 16, 16, 4) == -2
+
+
+def test_gemv_ex_rejects(lib):
+    f = lib.seedmm_gemv_ex
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 7, 16, FAKE, 16, 16, 16, 4, 1, None) == -1   # dtype
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 1, 8, FAKE, 16, 16, 16, 4, 1, None) == -1    # ldx < K
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 1, 16, FAKE, 8, 16, 16, 4, 1, None) == -1    # ldy < M
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 1, 20, FAKE, 16, 16, 16, 4, 2, None) == -2   # bf16 ldx % 8
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 0, 18, FAKE, 16, 16, 16, 4, 2, None) == -2   # f32 ldx % 4
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 1, 16, FAKE, 16, 16, 16, 4, -1, None) == -1  # N < 0
+    # empty problems are a no-op success
+    assert f(None, None, None, 0, None, 1, 16, None, 16, 0, 16, 4, 4, None) == 0
+    assert f(None, None, None, 0, None, 1, 16, None, 16, 16, 16, 4, 0, None) == 0
+
+
+def test_reconstruct_rejects(lib):
+    f = lib.seedmm_reconstruct
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 3, 16, 16, 4, None) == -1     # dtype
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 0, 16, 15, 4, None) == -1     # K
+    assert f(FAKE, FAKE, FAKE, 0, FAKE + 2, 0, 16, 16, 4, None) == -2  # W alignment
+    assert f(None, None, None, 0, None, 0, 0, 16, 4, None) == 0       # empty
+
+
+def _mat():
+    from pseudo_random_weight_amd.seedmm import SeedMat
+    return SeedMat(FAKE, FAKE, FAKE, FAKE)
+
+
+def test_moe_rejects_and_workspace(lib):
+    f = lib.seedmm_moe
+    ws = lib.seedmm_moe_workspace_bytes(64, 8, 100, 2048, 1024)
+    assert ws > 64 * 8 * (1024 * 2 + 2048 * 4)
+    assert lib.seedmm_moe_workspace_bytes(128, 8, 100, 2048, 1024) > ws
+    assert lib.seedmm_moe_workspace_bytes(-1, 8, 100, 2048, 1024) == 0
+    m = _mat()
+    args = lambda T=4, k=2, E=8, H=64, I=32, P=4, wsb=ws, x=FAKE: (
+        FAKE, FAKE, T, k, x, FAKE, E, H, I, P, m, m, m, FAKE, wsb, None)
+    assert f(*args(k=9)) == -1               # top_k > E
+    assert f(*args(k=0)) == -1
+    assert f(*args(H=60)) == -1              # H % 8
+    assert f(*args(P=5)) == -1
+    assert f(*args(E=0)) == -1
+    assert f(*args(wsb=16)) == -3            # workspace too small
+    assert f(*args(x=FAKE + 2)) == -2        # x misaligned
+    assert f(*args(T=0)) == 0                # empty batch: no-op
+
+
+def test_dispatch_rejects(lib):
+    assert lib.seedmm_moe_dispatch(FAKE, 4, 0, 8, FAKE, FAKE, None) == -1
+    assert lib.seedmm_moe_dispatch(FAKE, -1, 2, 8, FAKE, FAKE, None) == -1
+    assert lib.seedmm_moe_dispatch(FAKE, 4, 2, 0, FAKE, FAKE, None) == -1
+
+
+def test_binding_has_no_fallback():
+    src = open(os.path.join(ROOT, "pseudo_random_weight_amd", "seedmm.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+    assert "raise ImportError" in src

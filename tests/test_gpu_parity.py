@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Weights are compared bit for bit; products by relative L2 error
+||y - y_ref|| / ||y_ref|| (fp32 activations: 1e-5; bf16 activations with fp32
+accumulation: 1e-2).  Full-size workloads are checked on sampled outputs the oracle
+computes one token at a time.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def sm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from pseudo_random_weight_amd import seedmm
+    return seedmm
+
+
+def dev(mat):
+    import torch
+    return {
+        "seeds": torch.from_numpy(mat["seeds"].view(np.int16).copy()).view(torch.uint16).cuda(),
+        "coefs": torch.from_numpy(mat["coefs"].view(np.int16).copy()).view(torch.uint16).cuda(),
+        "codes": torch.from_numpy(mat["codes"].copy()).cuda(),
+        "exp_bias": torch.from_numpy(mat["exp_bias"].copy()).cuda(),
+        "exp_bias_host": mat["exp_bias"].copy(),
+    }
+
+
+def rel_l2(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def bf16_tensor(xf32):
+    import torch
+    bits = synth.bf16_bits(xf32)
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda(), \
+        synth.bf16_bits_to_f32(bits)
+
+
+SHAPES = [
+    (256, 512),      # the small parity workload (vector path)
+    (37, 104),       # ragged rows, K not a multiple of 64 (per-block path)
+    (48, 8),         # a single block per row
+    (130, 2048),     # many segments, ragged row tile
+    (64, 576),       # K % 64 == 0 but not a multiple of the 4-quarter stride
+]
+
+
+@pytest.mark.parametrize("P", [4, 3])
+@pytest.mark.parametrize("M,K", SHAPES)
+def test_reconstruct_is_bit_exact(sm, oracle, P, M, K):
+    import torch
+    say("reconstruct", M, K, P)
+    mat = synth.seed_matrix(synth.config_seed(0), f"rc{M}x{K}", M, K, P)
+    d = dev(mat)
+    W = sm.reconstruct(d, M, K, P, torch.float32)
+    Wb = sm.reconstruct(d, M, K, P, torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.reconstruct_f32(mat, M, K, P)
+    refb = oracle.reconstruct_bf16(mat, M, K, P)
+    np.testing.assert_array_equal(W.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    np.testing.assert_array_equal(Wb.cpu().view(torch.int16).numpy().view(np.uint16), refb)
+
+
+def test_reconstruct_extreme_exponents(sm, oracle):
+    import torch
+    say("reconstruct exponents")
+    M, K, P = 16, 256, 4
+    for eb in (-100, -4, 0, 37, 100):
+        mat = synth.seed_matrix(synth.config_seed(0), f"eb{eb}", M, K, P, exp_bias=eb)
+        W = sm.reconstruct(dev(mat), M, K, P, torch.float32)
+        torch.cuda.synchronize()
+        ref = oracle.reconstruct_f32(mat, M, K, P)
+        np.testing.assert_array_equal(W.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("P", [4, 3])
+@pytest.mark.parametrize("M,K", SHAPES)
+def test_gemv_fp32_matches_oracle(sm, oracle, P, M, K):
+    import torch
+    say("gemv fp32", M, K, P)
+    base = synth.config_seed(0)
+    mat = synth.seed_matrix(base, f"gv{M}x{K}", M, K, P)
+    x = synth.normal_f32(base, f"x{K}", (K,))
+    y = sm.gemv(dev(mat), torch.from_numpy(x).cuda(), M, K, P)
+    torch.cuda.synchronize()
+    ref = oracle.gemv(mat, x[None], M, K, P)[0]
+    assert rel_l2(y.cpu().numpy(), ref) <= 1e-5
+
+
+def test_gemv_one_hot_is_bit_exact(sm, oracle):
+    import torch
+    say("gemv one-hot")
+    M, K, P = 256, 512, 4
+    mat = synth.seed_matrix(synth.config_seed(0), "onehot", M, K, P)
+    d = dev(mat)
+    Wref = oracle.reconstruct_f32(mat, M, K, P)
+    for k in (0, 5, 8, 263, 511):
+        x = torch.zeros(K, dtype=torch.float32, device="cuda")
+        x[k] = 1.0
+        y = sm.gemv(d, x, M, K, P)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), Wref[:, k])
+
+
+@pytest.mark.parametrize("N", [2, 3, 5, 9])
+def test_gemv_ex_fp32_batches(sm, oracle, N):
+    import torch
+    say("gemv_ex fp32", N)
+    M, K, P = 96, 1024, 4
+    base = synth.config_seed(0)
+    mat = synth.seed_matrix(base, "gvb", M, K, P)
+    x = synth.normal_f32(base, f"xb{N}", (N, K))
+    y = sm.gemv_ex(dev(mat), torch.from_numpy(x).cuda(), M, K, P)
+    torch.cuda.synchronize()
+    ref = oracle.gemv(mat, x, M, K, P)
+    assert rel_l2(y.cpu().numpy(), ref) <= 1e-5
+    # linearity: W (a + b) = W a + W b up to rounding
+    y2 = sm.gemv_ex(dev(mat), torch.from_numpy(2 * x).cuda(), M, K, P)
+    torch.cuda.synchronize()
+    assert rel_l2(y2.cpu().numpy(), 2 * ref) <= 1e-5
+
+
+@pytest.mark.parametrize("P", [4, 3])
+@pytest.mark.parametrize("N", [1, 8, 16, 17, 64, 65, 300])
+def test_gemv_ex_bf16_matches_oracle(sm, oracle, P, N):
+    import torch
+    say("gemv_ex bf16", N, P)
+    M, K = 160, 768
+    base = synth.config_seed(1)
+    mat = synth.seed_matrix(base, f"gx{P}", M, K, P)
+    xt, x32 = bf16_tensor(synth.normal_f32(base, f"xx{N}", (N, K)))
+    y = sm.gemv_ex(dev(mat), xt, M, K, P)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref = oracle.gemv(mat, x32, M, K, P)
+    assert rel_l2(y, ref) <= 1e-2
+    # the kernel multiplies the bf16 (nearest-even) weights exactly with fp32 sums
+    Wb = synth.bf16_bits_to_f32(oracle.reconstruct_bf16(mat, M, K, P)).astype(np.float64)
+    ref_b = x32.astype(np.float64) @ Wb.T
+    assert rel_l2(y, ref_b) <= 1e-5
+
+
+def test_dispatch_groups_pairs_in_order(sm):
+    import torch
+    for (T, E, k) in [(1, 100, 8), (64, 100, 8), (37, 5, 3), (4096, 100, 8), (3, 16, 1)]:
+        say("dispatch", T, E, k)
+        ids, _ = synth.route_topk(synth.config_seed(2), f"d{T}", T, E, k)
+        counts, lists = sm.moe_dispatch(torch.from_numpy(ids).cuda(), E)
+        torch.cuda.synchronize()
+        counts = counts.cpu().numpy()
+        lists = lists.cpu().numpy()
+        flat = ids.reshape(-1)
+        np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+        for e in range(E):
+            np.testing.assert_array_equal(lists[e, :counts[e]], np.nonzero(flat == e)[0])
+
+
+_LAYERS = {}
+
+
+def layer(E, H, I, P, cfg):
+    """Seed-coded gate/up/down stacks of one layer (cached: the 100-expert layer is large)."""
+    key = (E, H, I, P, cfg)
+    if key not in _LAYERS:
+        base = synth.config_seed(cfg)
+        _LAYERS[key] = (synth.seed_matrix(base, "gate", I, H, P, E),
+                        synth.seed_matrix(base, "up", I, H, P, E),
+                        synth.seed_matrix(base, "down", H, I, P, E))
+    return _LAYERS[key]
+
+
+def moe_case(T, E, H, I, P, k, cfg, tag):
+    base = synth.config_seed(cfg)
+    gate, up, down = layer(E, H, I, P, cfg)
+    ids, w = synth.route_topk(base, tag + ".router", T, E, k)
+    x = synth.normal_f32(base, tag + ".x", (T, H))
+    return gate, up, down, ids, w, x
+
+
+def run_moe(sm, gate, up, down, ids, w, x, E, H, I, P):
+    import torch
+    xt, x32 = bf16_tensor(x)
+    y = sm.moe(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), xt, E, H, I, P,
+               dev(gate), dev(up), dev(down))
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), x32
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_single_expert_ffn(sm, oracle, T):
+    # one SwiGLU expert, hidden 2048, intermediate 768, P=4 (top-1 routing, weight 1)
+    say("expert ffn", T)
+    E, H, I, P = 1, 2048, 768, 4
+    gate, up, down, _, _, x = moe_case(T, E, H, I, P, 1, 1, "ffn")
+    ids = np.zeros((T, 1), dtype=np.int32)
+    w = np.ones((T, 1), dtype=np.float32)
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    ref = oracle.expert(gate, up, down, x32, H, I, P)
+    assert rel_l2(y, ref) <= 1e-2
+
+
+@pytest.mark.parametrize("P,T", [(4, 1), (4, 4), (3, 1)])
+def test_moe_layer_full(sm, oracle, P, T):
+    # the 100-expert layer, 2048 -> 1024 -> 2048, top-8, every output checked
+    say("moe full", P, T)
+    E, H, I, k = 100, 2048, 1024, 8
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2 if P == 4 else 3, f"moe{P}")
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
+    assert rel_l2(y, ref) <= 1e-2
+
+
+@pytest.mark.parametrize("P,T", [(4, 16), (4, 64), (3, 16)])
+def test_moe_layer_sampled_tokens(sm, oracle, P, T):
+    say("moe sampled", P, T)
+    E, H, I, k = 100, 2048, 1024, 8
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2 if P == 4 else 3, f"moeS{P}")
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    for t in (0, T // 2, T - 1):
+        ref = oracle.moe(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, P, gate, up, down)
+        assert rel_l2(y[t], ref[0]) <= 1e-2, t
+
+
+def test_moe_prefill_path_small(sm, oracle):
+    # >= 64 tokens per expert selects the prefill shape; small dims keep the oracle quick
+    say("moe prefill small")
+    T, E, H, I, P, k = 600, 8, 256, 128, 4, 2
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 4, "pfs")
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
+    assert rel_l2(y, ref) <= 1e-2
+
+
+def test_moe_prefill_full_size_sampled(sm, oracle):
+    # 4096 tokens through the 100-expert top-8 layer; sampled tokens vs the oracle
+    say("moe prefill 4096")
+    T, E, H, I, P, k = 4096, 100, 2048, 1024, 4, 8
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 4, "pf")
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    assert np.all(np.isfinite(y))
+    for t in (0, 1234, T - 1):
+        ref = oracle.moe(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, P, gate, up, down)
+        assert rel_l2(y[t], ref[0]) <= 1e-2, t
+
+
+def test_moe_edge_cases(sm, oracle):
+    import torch
+    E, H, I, P = 6, 192, 96, 4        # H, I not multiples of 64: per-block path
+    gate, up, down, ids, w, x = moe_case(40, E, H, I, P, 2, 5, "edge")
+    say("moe all tokens to one expert")
+    ids1 = np.full((40, 1), 3, dtype=np.int32)
+    w1 = np.ones((40, 1), dtype=np.float32)
+    y, x32 = run_moe(sm, gate, up, down, ids1, w1, x, E, H, I, P)
+    ref = oracle.moe(ids1, w1, x32, E, H, I, P, gate, up, down)
+    assert rel_l2(y, ref) <= 1e-2
+    say("moe ragged dims, several experts empty")
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
+    assert rel_l2(y, ref) <= 1e-2
+    say("moe empty batch")
+    yt = sm.moe(torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
+                torch.zeros((0, 2), dtype=torch.float32, device="cuda"),
+                torch.zeros((0, H), dtype=torch.bfloat16, device="cuda"), E, H, I, P,
+                dev(gate), dev(up), dev(down))
+    assert yt.shape == (0, H)
+
+
+def test_moe_is_deterministic_and_permutation_equivariant(sm):
+    say("moe determinism")
+    E, H, I, P, k, T = 100, 2048, 1024, 4, 8, 16
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2, "det")
+    y1, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    y2, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    np.testing.assert_array_equal(y1, y2)
+    perm = np.random.default_rng(0).permutation(T)
+    y3, _ = run_moe(sm, gate, up, down, ids[perm], w[perm], x[perm], E, H, I, P)
+    np.testing.assert_array_equal(y3, y1[perm])
