@@ -1,0 +1,270 @@
+#!/usr/bin/env python
+"""Benchmark of the seed-decoding MoE layer on one MI355X.
+
+A step is one decode pass of a routed mixture-of-experts layer whose expert weights
+are SeedLM seeds: 100 SwiGLU experts 2048 -> 1024 -> 2048, P = 4, top-8 softmax
+routing, T bf16 tokens (default 64): dispatch, fused gate/up + SwiGLU, down, ordered
+combine.  Inputs are synthetic (seeded generator), resident in HBM before timing;
+routing and activations are fresh every step and the weights rotate over replicas so
+every step reads its compressed weights from HBM, not from the 256 MB Infinity Cache.
+
+Prints one JSON line: effective weights/s (distinct expert weights applied per second),
+compressed HBM GB/s and its fraction of 8 TB/s, decode tokens/s, the roofline of the
+dominant kernel (fused gate/up) from HIP events inside the timed region, and the CPU
+oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective weights/s + compressed HBM GB/s (% roofline); MoE-layer decode tok/s"
+HBM_PEAK = 8.0e12                 # bytes/s, MI355X HBM3E
+VALU_PEAK = 256 * 4 * 16 * 2.4e9  # lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+E, H, I, TOPK = 100, 2048, 1024, 8
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=64, help="decode batch T")
+    ap.add_argument("--P", type=int, default=4, choices=(3, 4))
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the T = 1, 4, 16 lines")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def compressed_bytes_per_matrix(P):
+    nblk = H * I // 8
+    return nblk * 2 + (nblk * P + 3) // 4 * 2 + (nblk + 1) // 2
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from the committed counter summary, if it still matches the
+    kernel sources (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("seedmm.hip", "seed_decode.hpp"):
+        with open(os.path.join(ROOT, "pseudo_random_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != digest:
+        return None
+    key = f"{kernel_tag}.bytes_per_launch"
+    return float(vals[key]) if key in vals else None
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime (the library records them between its
+    kernels; torch's Event wrapper cannot time events it did not record itself)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.live = []
+
+    def create(self):
+        h = self.ct.c_void_p()
+        rc = self.hip.hipEventCreate(self.ct.byref(h))
+        assert rc == 0, f"hipEventCreate failed ({rc})"
+        self.live.append(h.value)
+        return h.value
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return out.value
+
+    def close(self):
+        for h in self.live:
+            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+        self.live = []
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from pseudo_random_weight_amd import seedmm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    P, T = args.P, args.tokens
+    base = synth.config_seed(2 if P == 4 else 3)
+
+    def to_dev(m):
+        return {"seeds": torch.from_numpy(m["seeds"].view(np.int16)).view(torch.uint16).to(dev),
+                "coefs": torch.from_numpy(m["coefs"].view(np.int16)).view(torch.uint16).to(dev),
+                "codes": torch.from_numpy(m["codes"]).to(dev),
+                "exp_bias": torch.from_numpy(m["exp_bias"]).to(dev)}
+
+    hipev = HipEvents()
+    host = {n: synth.seed_matrix(base, n, *( (I, H) if n != "down" else (H, I) ), P, E)
+            for n in ("gate", "up", "down")}
+    reps = []
+    first = {n: to_dev(m) for n, m in host.items()}
+    reps.append(first)
+    for _ in range(args.replicas - 1):
+        reps.append({n: {k: v.clone() for k, v in m.items()} for n, m in first.items()})
+    layer_bytes = 3 * E * compressed_bytes_per_matrix(P)
+
+    nsteps_total = args.warmup + args.steps
+
+    def make_batches(T, n):
+        ids, ws, xs = [], [], []
+        for s in range(n):
+            i, w = synth.route_topk(base, f"router.T{T}.s{s}", T, E, TOPK)
+            x = synth.bf16_bits(synth.normal_f32(base, f"x.T{T}.s{s}", (T, H)))
+            ids.append(i), ws.append(w), xs.append(x)
+        return (torch.from_numpy(np.stack(ids)).to(dev), torch.from_numpy(np.stack(ws)).to(dev),
+                torch.from_numpy(np.stack(xs).view(np.int16)).view(torch.bfloat16).to(dev),
+                ids)
+
+    if args.calib_copy_mb:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def run(T, warmup, steps, timed_events=True):
+        ids_d, w_d, x_d, ids_h = make_batches(T, warmup + steps)
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(seedmm.moe_workspace_bytes(T, TOPK, E, H, I), dtype=torch.uint8,
+                         device=dev)
+        evs = [[hipev.create() for _ in range(5)] for _ in range(steps)]
+
+        def step(s, ev=None):
+            r = reps[s % len(reps)]
+            seedmm.moe(ids_d[s], w_d[s], x_d[s], E, H, I, P, r["gate"], r["up"], r["down"],
+                       y=y, workspace=ws, events=ev)
+
+        for s in range(warmup):
+            step(s)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            step(warmup + s, evs[s] if timed_events else None)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stages = np.zeros(4)
+        if timed_events:
+            for s in range(steps):
+                for j in range(4):
+                    stages[j] += hipev.ms(evs[s][j], evs[s][j + 1]) * 1e-3
+            stages /= steps
+        distinct = [len(np.unique(ids_h[warmup + s])) for s in range(steps)]
+        return wall / steps, stages, np.array(distinct, dtype=np.float64), ids_h, x_d, w_d
+
+    t_step, stages, distinct, ids_h, x_d, w_d = run(T, args.warmup, args.steps)
+    w_per_mat = H * I
+    weights = distinct.mean() * 3 * w_per_mat
+    cbytes = distinct.mean() * 3 * compressed_bytes_per_matrix(P)
+    value = weights / t_step
+    gbps = cbytes / t_step
+
+    # dominant kernel: fused gate/up (two thirds of the weights)
+    t_gu = stages[1]
+    gu_weights = distinct.mean() * 2 * w_per_mat
+    alg_ops = gu_weights * (2 * P + 1)       # P states + P integer MACs + 1 scale per weight
+    traffic = read_traffic("gateup_T%d_P%d" % (T, P))
+    roofline = {"bound": "alu", "achieved": alg_ops / t_gu, "peak": VALU_PEAK,
+                "unit": "lane-op/s", "frac": alg_ops / t_gu / VALU_PEAK,
+                "traffic": traffic,
+                "kernel": "k_mfma<GATEUP> (fused gate/up + SwiGLU)",
+                "alg_ops_per_weight": 2 * P + 1,
+                "kernel_us": t_gu * 1e6,
+                "compressed_bytes_per_launch": distinct.mean() * 2 * compressed_bytes_per_matrix(P),
+                "hbm_frac_compressed": distinct.mean() * 2 * compressed_bytes_per_matrix(P)
+                / t_gu / HBM_PEAK}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "weights/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "moe_layer_decode", "experts": E, "top_k": TOPK, "hidden": H,
+                   "intermediate": I, "P": P, "tokens": T, "activations": "bf16",
+                   "weight_replicas": args.replicas, "layer_compressed_MB": layer_bytes / 1e6},
+        "compressed_GBps": gbps / 1e9, "hbm_frac": gbps / HBM_PEAK, "tok_s": T / t_step,
+        "distinct_experts_per_step": distinct.mean(),
+        "stage_us": {"dispatch": stages[0] * 1e6, "gate_up": stages[1] * 1e6,
+                     "down": stages[2] * 1e6, "combine": stages[3] * 1e6},
+        "roofline": roofline,
+    }
+
+    if not args.no_sweep:
+        sweep = {}
+        for Ts in (1, 4, 16, 64):
+            if Ts == T:
+                continue
+            ts, st, dis, *_ = run(Ts, 3, 20)
+            sweep[str(Ts)] = {"ms_per_step": ts * 1e3, "tok_s": Ts / ts,
+                              "weights_per_s": dis.mean() * 3 * w_per_mat / ts,
+                              "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
+                              "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6}
+        out["by_batch"] = sweep
+
+    if not args.no_cpu:
+        import oracle
+        s0 = args.warmup
+        ids0 = ids_h[s0]
+        x0 = synth.bf16_bits_to_f32(x_d[s0].view(torch.int16).cpu().numpy().view(np.uint16))
+        w0 = w_d[s0].cpu().numpy()
+        t0 = time.perf_counter()
+        n = 0
+        while n < T and (time.perf_counter() - t0) < args.cpu_seconds:
+            oracle.moe(ids0[n:n + 1], w0[n:n + 1], x0[n:n + 1], E, H, I, P,
+                       host["gate"], host["up"], host["down"])
+            n += 1
+        t_cpu = (time.perf_counter() - t0) / n * T       # the oracle's cost is linear in tokens
+        d0 = len(np.unique(ids0))
+        out["cpu_baseline"] = {
+            "value": d0 * 3 * w_per_mat / t_cpu, "unit": "weights/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"oracle MoE on the first {n} of the {T} tokens of one step "
+                      f"({time.perf_counter() - t0:.1f} s), scaled linearly to the step",
+            "tok_s": T / t_cpu}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -141,6 +141,20 @@ int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
                seedmm_mat gate, seedmm_mat up, seedmm_mat down,
                void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * seedmm_moe_timed -- seedmm_moe that also records caller-created hipEvent_t handles on
+ * hip_stream between its kernels, for measuring each stage in place:
+ *   events[0] before the dispatch, events[1] after it, events[2] after the gate/up
+ *   kernel, events[3] after the down kernel, events[4] after the combine.
+ * `events` may be NULL and any entry may be NULL.  Same arguments, results and errors
+ * as seedmm_moe; no event is recorded when the arguments are rejected.
+ */
+int seedmm_moe_timed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                     const void *x, float *y, int E, int H, int I, int P,
+                     seedmm_mat gate, seedmm_mat up, seedmm_mat down,
+                     void *workspace, size_t workspace_bytes, void *hip_stream,
+                     void *const *events);
+
 /* Static description of a status code. */
 const char *seedmm_strerror(int status);
 

@@ -266,15 +266,138 @@ struct MfmaArgs {
     int ldy;
 };
 
+// Per-lane state of one pass over K.
+struct Lane {
+    Mat W1, W2;
+    int64_t rowb;        // first block of this lane's row (row clamped into range)
+    bool rv;             // the row exists
+    int nbpr, nseg, n_it, ks, q;
+};
+
+// One pass over K for NTA token tiles.  Branch-free: addresses are clamped into range
+// and padding blocks get all-zero coefficients, which decode to exact zero weights.
+template <int P, bool VEC, int NMAT, int NTA, int KSPLIT>
+__device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const* brow,
+                                            f32x4* acc, f32x4* acc2) {
+    constexpr int GSTRIDE = KSPLIT * 4;
+    for (int it = 0; it < L.n_it; ++it) {
+        const int g = it * GSTRIDE + L.ks * 4 + L.q;
+        const bool gv = g < L.nseg && L.rv;
+        const int gc = g < L.nseg ? g : L.nseg - 1;
+        const int nvalid = gv ? min(8, L.nbpr - gc * 8) : 0;
+        Seg<P, VEC> s1, s2;
+        s1.load(L.W1.seeds, L.W1.coefs, L.W1.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
+        if constexpr (NMAT == 2)
+            s2.load(L.W2.seeds, L.W2.coefs, L.W2.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const bool bv = s < nvalid;
+            const int kb = min(gc * 8 + s, L.nbpr - 1);
+            float w[8];
+            decode_block<P>(lfsr_window(s1.seed(s)), bv ? s1.coef(s) : 0u, s1.code(s),
+                            L.W1.exp_bias, w);
+            const bf16x8 A = pack_bf16(w);
+            bf16x8 A2;
+            if constexpr (NMAT == 2) {
+                decode_block<P>(lfsr_window(s2.seed(s)), bv ? s2.coef(s) : 0u, s2.code(s),
+                                L.W2.exp_bias, w);
+                A2 = pack_bf16(w);
+            }
+#pragma unroll
+            for (int t = 0; t < NTA; ++t) {
+                const bf16x8 B = load_bf16x8(brow[t] + 8 * kb);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
+                if constexpr (NMAT == 2)
+                    acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc2[t], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// One pass: NTA tiles of 16 tokens starting at token slot `pass`.
+template <int P, bool VEC, int NTA, int MODE, int KSPLIT, int NT>
+__device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, const int32_t* list,
+                                          int n_e, int pass, int m0, int lane, int r,
+                                          f32x4 (*red)[NT * (MODE == MODE_GATEUP ? 2 : 1)][64]) {
+    constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
+    // B rows of this lane (token column r of every tile); slots past n_e repeat the last
+    // token so every load stays in range -- their outputs are never stored.
+    const uint16_t* brow[NTA];
+#pragma unroll
+    for (int t = 0; t < NTA; ++t) {
+        const int i = min(pass + 16 * t + r, n_e - 1);
+        int64_t src;
+        if constexpr (MODE == MODE_GEMM) src = i;
+        else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
+        else src = list[i];
+        brow[t] = a.x + src * a.ldx;
+    }
+    f32x4 acc[NTA], acc2[NTA];
+#pragma unroll
+    for (int t = 0; t < NTA; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    mfma_k_loop<P, VEC, NMAT, NTA, KSPLIT>(L, brow, acc, acc2);
+
+    if constexpr (KSPLIT > 1) {
+#pragma unroll
+        for (int t = 0; t < NTA; ++t) {
+            red[L.ks][t][lane] = acc[t];
+            if constexpr (NMAT == 2) red[L.ks][NT + t][lane] = acc2[t];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < NTA; ++t) {
+        if (KSPLIT > 1 && (t % KSPLIT) != L.ks) continue;
+        f32x4 v = acc[t], v2 = acc2[t];
+        if constexpr (KSPLIT > 1) {
+            v = red[0][t][lane];
+#pragma unroll
+            for (int w = 1; w < KSPLIT; ++w) v += red[w][t][lane];
+            if constexpr (NMAT == 2) {
+                v2 = red[0][NT + t][lane];
+#pragma unroll
+                for (int w = 1; w < KSPLIT; ++w) v2 += red[w][NT + t][lane];
+            }
+        }
+        const int i = pass + 16 * t + r;     // D column = token slot
+        if (i >= n_e) continue;
+        int64_t dst;
+        float scale = 1.0f;
+        if constexpr (MODE == MODE_GEMM) {
+            dst = i;
+        } else {
+            dst = list[i];
+            if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
+        }
+        const int mq = m0 + 4 * (lane >> 4);   // D rows mq .. mq+3
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = mq + j;
+            if (m >= a.M) continue;
+            if constexpr (MODE == MODE_GATEUP) {
+                const float gt = v[j], up = v2[j];
+                const float hv = gt / (1.0f + expf(-gt)) * up;
+                const __bf16 hb = (__bf16)hv;
+                a.h[dst * a.ldy + m] = __builtin_bit_cast(uint16_t, hb);
+            } else {
+                a.y[dst * a.ldy + m] = scale * v[j];
+            }
+        }
+    }
+    if constexpr (KSPLIT > 1) __syncthreads();
+}
+
 template <int P, bool VEC, int NT, int MODE, int KSPLIT>
 __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
     constexpr int ROWT = 4 / KSPLIT;
     constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
-    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][KSPLIT > 1 ? NT * NMAT : 1][64];
+    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][NT * NMAT][64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, q = lane >> 4;
-    const int ks = wave % KSPLIT, rt = wave / KSPLIT;
+    const int r = lane & 15;
 
     // ---- which expert this workgroup serves --------------------------------------
     int e = 0, n_e = a.N;
@@ -300,136 +423,41 @@ __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
         n_e = a.counts[e];
         list = a.lists + (int64_t)e * a.T;
     }
+    if (n_e <= 0) return;
 
-    const int M = a.M, K = a.K;
-    const int nbpr = K / 8;
-    const int64_t nblk = (int64_t)M * nbpr;
-    const Mat W1 = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
-    Mat W2 = W1;
-    if constexpr (MODE == MODE_GATEUP) W2 = mat_of(a.A2, e, nblk, P, 0, true);
-
+    Lane L;
+    L.ks = wave % KSPLIT;
+    L.q = lane >> 4;
+    const int rt = wave / KSPLIT;
+    L.nbpr = a.K / 8;
+    const int64_t nblk = (int64_t)a.M * L.nbpr;
+    L.W1 = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
+    L.W2 = L.W1;
+    if constexpr (MODE == MODE_GATEUP) L.W2 = mat_of(a.A2, e, nblk, P, 0, true);
     const int m0 = (blockIdx.x * ROWT + rt) * 16;
     const int row = m0 + r;
-    const bool rv = row < M;
-    const int64_t rowb = (int64_t)(rv ? row : 0) * nbpr;
-    const int nseg = (nbpr + 7) / 8;
-    constexpr int GSTRIDE = KSPLIT * 4;
-    const int n_it = (nseg + GSTRIDE - 1) / GSTRIDE;
+    L.rv = row < a.M;
+    L.rowb = (int64_t)(L.rv ? row : a.M - 1) * L.nbpr;
+    L.nseg = (L.nbpr + 7) / 8;
+    L.n_it = (L.nseg + KSPLIT * 4 - 1) / (KSPLIT * 4);
 
     for (int pass = 0; pass < n_e; pass += NT * 16) {
-        const int ntiles = min(NT, (n_e - pass + 15) / 16);
-        // B rows of this lane: token column r of every tile
-        const uint16_t* brow[NT];
-        bool bv[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int i = pass + 16 * t + r;
-            bv[t] = i < n_e;
-            int64_t src = 0;
-            if (bv[t]) {
-                if constexpr (MODE == MODE_GEMM) src = i;
-                else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
-                else src = list[i];
+        const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
+        if constexpr (NT == 4) {
+            switch (ntiles) {
+                case 1: mfma_pass<P, VEC, 1, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+                case 2: mfma_pass<P, VEC, 2, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+                case 3: mfma_pass<P, VEC, 3, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+                default: mfma_pass<P, VEC, 4, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
             }
-            brow[t] = a.x + src * a.ldx;
+        } else {
+            // long token lists: full passes of NT tiles; the tail pass rounds up to a
+            // multiple of 4 tiles (extra columns repeat a valid token, never stored)
+            if (ntiles > NT - 4 || NT <= 4) mfma_pass<P, VEC, NT, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
+            else if (ntiles > 8) mfma_pass<P, VEC, 12, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
+            else if (ntiles > 4) mfma_pass<P, VEC, 8, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
+            else mfma_pass<P, VEC, 4, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
         }
-
-        f32x4 acc[NT], acc2[NMAT == 2 ? NT : 1];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < (NMAT == 2 ? NT : 1); ++t) acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int it = 0; it < n_it; ++it) {
-            const int g = it * GSTRIDE + ks * 4 + q;
-            const bool gv = g < nseg;
-            const int nvalid = gv ? min(8, nbpr - g * 8) : 0;
-            Seg<P, VEC> s1, s2;
-            if (gv && rv) {
-                s1.load(W1.seeds, W1.coefs, W1.codes, rowb + g * 8, nvalid);
-                if constexpr (NMAT == 2) s2.load(W2.seeds, W2.coefs, W2.codes, rowb + g * 8, nvalid);
-            }
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int kb = g * 8 + s;
-                const bool kv = s < nvalid;
-                bf16x8 A = zero_bf16x8(), A2 = zero_bf16x8();
-                if (kv && rv) {
-                    float w[8];
-                    decode_block<P>(lfsr_window(s1.seed(s)), s1.coef(s), s1.code(s),
-                                    W1.exp_bias, w);
-                    A = pack_bf16(w);
-                    if constexpr (NMAT == 2) {
-                        decode_block<P>(lfsr_window(s2.seed(s)), s2.coef(s), s2.code(s),
-                                        W2.exp_bias, w);
-                        A2 = pack_bf16(w);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    if (t < ntiles) {
-                        bf16x8 B = zero_bf16x8();
-                        if (kv && bv[t]) B = load_bf16x8(brow[t] + 8 * kb);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
-                        if constexpr (NMAT == 2)
-                            acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc2[t], 0, 0, 0);
-                    }
-                }
-            }
-        }
-
-        // ---- reduce the K split and write -------------------------------------------
-        if constexpr (KSPLIT > 1) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (t < ntiles) {
-                    red[ks][t][lane] = acc[t];
-                    if constexpr (NMAT == 2) red[ks][NT + t][lane] = acc2[t];
-                }
-            }
-            __syncthreads();
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t >= ntiles) continue;
-            if (KSPLIT > 1 && (t % KSPLIT) != ks) continue;
-            f32x4 v = acc[t], v2 = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (NMAT == 2) v2 = acc2[t];
-            if constexpr (KSPLIT > 1) {
-                v = red[0][t][lane];
-#pragma unroll
-                for (int w = 1; w < KSPLIT; ++w) v += red[w][t][lane];
-                if constexpr (NMAT == 2) {
-                    v2 = red[0][NT + t][lane];
-#pragma unroll
-                    for (int w = 1; w < KSPLIT; ++w) v2 += red[w][NT + t][lane];
-                }
-            }
-            const int i = pass + 16 * t + r;     // D column = token slot
-            if (i >= n_e) continue;
-            int64_t dst;
-            float scale = 1.0f;
-            if constexpr (MODE == MODE_GEMM) {
-                dst = i;
-            } else {
-                dst = list[i];
-                if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m = m0 + 4 * q + j;   // D row
-                if (m >= M) continue;
-                if constexpr (MODE == MODE_GATEUP) {
-                    const float gt = v[j], up = v2[j];
-                    const float hv = gt / (1.0f + expf(-gt)) * up;
-                    const __bf16 hb = (__bf16)hv;
-                    a.h[dst * a.ldy + m] = __builtin_bit_cast(uint16_t, hb);
-                } else {
-                    a.y[dst * a.ldy + m] = scale * v[j];
-                }
-            }
-        }
-        if constexpr (KSPLIT > 1) __syncthreads();
     }
 }
 
@@ -663,9 +691,10 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I) {
     return L.total;
 }
 
-int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
-               float* y, int E, int H, int I, int P, seedmm_mat gate, seedmm_mat up,
-               seedmm_mat down, void* workspace, size_t workspace_bytes, void* hip_stream) {
+int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int top_k,
+                     const void* x, float* y, int E, int H, int I, int P, seedmm_mat gate,
+                     seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
+                     void* hip_stream, void* const* events) {
     if (T < 0 || E < 1 || E > 4096 || top_k < 1 || top_k > E || top_k > 64) return SEEDMM_EINVAL;
     if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0 || (P != 3 && P != 4)) return SEEDMM_EINVAL;
     const int64_t nblk = (int64_t)I * (H / 8);   // blocks of one gate/up/down matrix
@@ -687,7 +716,12 @@ int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, c
     uint16_t* hbuf = (uint16_t*)(ws + L.h);
     float* obuf = (float*)(ws + L.o);
 
+    auto mark = [&](int i) {
+        if (events && events[i]) hipEventRecord((hipEvent_t)events[i], st);
+    };
+    mark(0);
     hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T, counts, lists);
+    mark(1);
 
     const int pairs = T * top_k;
     const int gridy = pairs < E ? pairs : E;          // at most this many active experts
@@ -703,6 +737,7 @@ int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, c
     a.counts = counts; a.lists = lists; a.E = E; a.T = T; a.top_k = top_k;
     a.h = hbuf; a.ldy = I;
     mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
+    mark(2);
 
     MfmaArgs b = {};
     b.A = down;
@@ -711,12 +746,20 @@ int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, c
     b.counts = counts; b.lists = lists; b.E = E; b.T = T; b.top_k = top_k;
     b.topk_w = topk_w; b.y = obuf; b.ldy = H;
     mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
+    mark(3);
 
     const int64_t n4 = (int64_t)T * (H / 4);
-    if (H % 4 != 0) return SEEDMM_EINVAL;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, obuf,
                        top_k, y, H, T);
+    mark(4);
     return launch_status();
+}
+
+int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
+               float* y, int E, int H, int I, int P, seedmm_mat gate, seedmm_mat up,
+               seedmm_mat down, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return seedmm_moe_timed(topk_ids, topk_w, T, top_k, x, y, E, H, I, P, gate, up, down,
+                            workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 }  // extern "C"

@@ -45,11 +45,12 @@ def _load():
     L.seedmm_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.seedmm_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, SeedMat, SeedMat, SeedMat,
                              p, ctypes.c_size_t, p]
+    L.seedmm_moe_timed.argtypes = L.seedmm_moe.argtypes + [p]
     L.seedmm_strerror.restype = ctypes.c_char_p
     L.seedmm_strerror.argtypes = [i32]
     L.seedmm_version.restype = i32
     for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-                 "seedmm_moe"):
+                 "seedmm_moe", "seedmm_moe_timed"):
         getattr(L, name).restype = i32
     return L
 
@@ -57,7 +58,8 @@ def _load():
 _lib = _load()
 
 EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_strerror", "seedmm_version")
+           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_strerror",
+           "seedmm_version")
 
 
 def lib():
@@ -168,8 +170,11 @@ def _seedmat(m: dict) -> SeedMat:
                    m["exp_bias"].data_ptr())
 
 
-def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None, stream=None):
-    """Routed SwiGLU MoE layer (seedmm_moe); x bf16 [T][H] -> y fp32 [T][H]."""
+def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None, stream=None,
+        events=None):
+    """Routed SwiGLU MoE layer (seedmm_moe); x bf16 [T][H] -> y fp32 [T][H].
+    `events`: optional 5 raw hipEvent_t handles (ints) recorded between the stages
+    (seedmm_moe_timed)."""
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")
@@ -180,8 +185,12 @@ def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None,
     need = moe_workspace_bytes(T, k, E, H, I)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _check(_lib.seedmm_moe(_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I, P,
-                           _seedmat(gate), _seedmat(up), _seedmat(down), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(stream)),
-           "seedmm_moe")
+    args = (_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I, P,
+            _seedmat(gate), _seedmat(up), _seedmat(down), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        _check(_lib.seedmm_moe(*args), "seedmm_moe")
+    else:
+        arr = (ctypes.c_void_p * 5)(*[getattr(ev, "cuda_event", ev) for ev in events])
+        _check(_lib.seedmm_moe_timed(*args, arr), "seedmm_moe_timed")
     return y
