@@ -23,6 +23,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
+    # keep per-thread arrays in registers (the LDS budget belongs to the kernels' tiles)
+    "-mllvm", "-disable-promote-alloca-to-lds",
 ]
 
 

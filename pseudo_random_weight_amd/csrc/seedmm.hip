@@ -24,6 +24,9 @@ namespace seedmm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte register value.  HIP's uint4 is a struct whose copies lower to memcpy, which
+// keeps staging registers in scratch memory; the native vector type stays in VGPRs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { MODE_GEMM = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
 
@@ -443,50 +446,284 @@ __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
 
     for (int pass = 0; pass < n_e; pass += NT * 16) {
         const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
-        if constexpr (NT == 4) {
-            switch (ntiles) {
-                case 1: mfma_pass<P, VEC, 1, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-                case 2: mfma_pass<P, VEC, 2, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-                case 3: mfma_pass<P, VEC, 3, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-                default: mfma_pass<P, VEC, 4, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            }
-        } else {
-            // long token lists: full passes of NT tiles; the tail pass rounds up to a
-            // multiple of 4 tiles (extra columns repeat a valid token, never stored)
-            if (ntiles > NT - 4 || NT <= 4) mfma_pass<P, VEC, NT, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
-            else if (ntiles > 8) mfma_pass<P, VEC, 12, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
-            else if (ntiles > 4) mfma_pass<P, VEC, 8, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
-            else mfma_pass<P, VEC, 4, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red);
+        static_assert(NT == 4, "the decode kernel holds at most 4 token tiles");
+        switch (ntiles) {
+            case 1: mfma_pass<P, VEC, 1, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            case 2: mfma_pass<P, VEC, 2, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            case 3: mfma_pass<P, VEC, 3, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            default: mfma_pass<P, VEC, 4, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
         }
     }
 }
 
 // ----------------------------------------------------------------------------------
+// Wide-token products (prefill and long token lists), vector-load layouts only
+// (K % 256 == 0, 16-byte aligned streams).  A workgroup of 8 waves owns AR = 128 weight
+// rows (64 rows of gate and of up, or 128 rows of one matrix) for up to NC = 8*NTW*16
+// tokens, so each weight block is regenerated once per pass over its expert's tokens.
+// Per 32-k step (blocks 4s..4s+3 of every row, contiguous k):
+//   - each thread regenerates one block and writes its 8 bf16 weights to LDS (A tile);
+//   - the step's 64-byte slice of every token row is staged in LDS (B tile);
+//   - wave w multiplies the 8 A tiles with its NTW token tiles (16x16x32 bf16 MFMA),
+//     accumulators in registers.
+// A and B are double-buffered: while the matrix cores work on step s the vector ALUs
+// regenerate step s+1 and the next B slice is in flight.  The seed / coefficient / code
+// streams of each 32-block group are staged in LDS with 16-byte loads one group ahead;
+// a row's stream chunks are written and read by the four lanes of one quad, so the
+// same-wave LDS ordering makes them visible without a barrier.
+// Workgroups are numbered so that every row group of one expert lands on the same XCD
+// (workgroups are dealt to the 8 XCDs round-robin), keeping that expert's token rows in
+// one L2.
+// ----------------------------------------------------------------------------------
+template <int P, int MODE, int NTW>
+__global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
+    constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
+    constexpr int AR = 128;                   // A rows per workgroup
+    constexpr int RM = AR / NMAT;             // rows per matrix
+    constexpr int RT = RM / 16;               // row tiles per matrix
+    constexpr int NA = AR / 16;               // A tiles per step
+    constexpr int NC = 8 * NTW * 16;          // token slots per pass
+    constexpr int CW = 32 * P / 4;            // coefficient words per row per group
+    __shared__ u32x4 As[2][AR * 4];
+    __shared__ u32x4 Bs[2][NC * 4];
+    __shared__ uint16_t Ss[2][AR * 32];
+    __shared__ uint16_t Cs[2][AR * CW + 8];
+    __shared__ uint8_t Ds[2][AR * 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, q = lane >> 4;
+
+    // ---- XCD-aware numbering: consecutive work items share an XCD ------------------
+    const int total = gridDim.x * gridDim.y;
+    const int L = blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3, q8 = total >> 3, r8 = total & 7;
+    const int work = xcd * q8 + min(xcd, r8) + slot;
+    const int rg = work % gridDim.x;          // row group
+    const int target = work / gridDim.x;      // active-expert index
+
+    // ---- expert ------------------------------------------------------------------
+    int e = 0, n_e = a.N;
+    const int32_t* list = nullptr;
+    if constexpr (MODE != MODE_GEMM) {
+        int found = -1, cum = 0;
+        for (int base = 0; base < a.E && found < 0; base += 64) {
+            const int idx = base + lane;
+            const bool act = idx < a.E && a.counts[idx] > 0;
+            const uint64_t bal = __ballot(act);
+            const int c = __popcll(bal);
+            if (target < cum + c) {
+                const int k = target - cum;
+                const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+                const bool mine = act && __popcll(below) == k;
+                found = base + __ffsll((long long)__ballot(mine)) - 1;
+            }
+            cum += c;
+        }
+        if (found < 0) return;
+        e = found;
+        n_e = a.counts[e];
+        list = a.lists + (int64_t)e * a.T;
+    }
+    if (n_e <= 0) return;
+
+    const int M = a.M, K = a.K, nbpr = K / 8;
+    const int64_t nblk = (int64_t)M * nbpr;
+    const int m0 = rg * RM;
+    const int ngroups = nbpr / 32;            // K % 256 == 0
+    const int NS = ngroups * 8;
+
+    // ---- regeneration role: A row `arow` (matrix dmat, row drow), block lane dj ------
+    const int arow = tid >> 2, dj = tid & 3;
+    const int dmat = arow / RM, drow = arow % RM;
+    Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
+    if constexpr (NMAT == 2) {
+        if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true);
+    }
+    const bool drv = m0 + drow < M;
+    const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
+
+    // stream staging: chunk dj of this row's group (seeds: 4 x 16 B, P=4 coefs 4 x 16 B,
+    // P=3 coefs 3 x 16 B, codes 1 x 16 B)
+    u32x4 sreg_s, sreg_c, sreg_d;
+    auto stream_load = [&](int g) {
+        const int64_t b0 = drowb + 32 * g;    // first block of the group in this row
+        sreg_s = *reinterpret_cast<const u32x4*>(W.seeds + b0 + 8 * dj);
+        if (dj < P) sreg_c = *reinterpret_cast<const u32x4*>(W.coefs + (b0 * P) / 4 + 8 * dj);
+        if (dj == 0) sreg_d = *reinterpret_cast<const u32x4*>(W.codes + b0 / 2);
+        if (!drv) sreg_c = u32x4{0u, 0u, 0u, 0u};   // missing rows decode to zero
+    };
+    auto stream_store = [&](int buf) {
+        *reinterpret_cast<u32x4*>(&Ss[buf][arow * 32 + 8 * dj]) = sreg_s;
+        if (dj < P) *reinterpret_cast<u32x4*>(&Cs[buf][arow * CW + 8 * dj]) = sreg_c;
+        if (dj == 0) *reinterpret_cast<u32x4*>(&Ds[buf][arow * 16]) = sreg_d;
+    };
+    // regenerate block (step s) of this thread from the staged streams
+    auto regen = [&](int s, u32x4* dst) {
+        const int buf = (s >> 3) & 1;
+        const int bl = 4 * (s & 7) + dj;      // block within the group
+        const uint32_t seed = Ss[buf][arow * 32 + bl];
+        uint32_t cw;
+        if constexpr (P == 4) {
+            cw = Cs[buf][arow * CW + bl];
+        } else {
+            const int n = 3 * bl, sh = 4 * (n & 3);
+            const uint16_t* c = &Cs[buf][arow * CW + (n >> 2)];
+            cw = ((uint32_t)c[0] | ((uint32_t)c[1] << 16)) >> sh;
+        }
+        const uint32_t code = ((uint32_t)Ds[buf][arow * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
+        float w[8];
+        decode_block<P>(lfsr_window(seed), cw, code, W.exp_bias, w);
+        *dst = __builtin_bit_cast(u32x4, pack_bf16(w));
+    };
+
+    for (int pass = 0; pass < n_e; pass += NC) {
+        // B staging role: chunks tid + 512 u = (token slot, 16-byte piece)
+        const uint16_t* brow[NTW];
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            const int i = min(pass + ((tid + 512 * u) >> 2), n_e - 1);
+            int64_t src;
+            if constexpr (MODE == MODE_GEMM) src = i;
+            else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
+            else src = list[i];
+            brow[u] = a.x + src * a.ldx + 8 * dj;
+        }
+
+        f32x4 acc[NA][NTW];
+#pragma unroll
+        for (int x = 0; x < NA; ++x)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) acc[x][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // prologue: streams of groups 0 (staged) and 1 (in registers), step 0 A and B in
+        // LDS, step 1 B in flight.  B slices are loaded two steps ahead of their use,
+        // alternating between two register sets (the loop is unrolled by two steps).
+        stream_load(0);
+        stream_store(0);
+        if (ngroups > 1) stream_load(1);
+        u32x4 bA[NTW], bB[NTW];               // two register sets, named statically
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) bA[u] = *reinterpret_cast<const u32x4*>(brow[u]);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) bB[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32);
+        regen(0, &As[0][tid]);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) Bs[0][tid + 512 * u] = bA[u];
+        __syncthreads();
+
+// One 32-k step s: B of step s+2 into BNEXT (free since step s's slice is in LDS),
+// MFMAs on buffer s&1, then weights and B slice (BSTORE) of step s+1 into buffer s&1^1.
+#define SEEDMM_WIDE_STEP(S, BNEXT, BSTORE)                                                   \
+    {                                                                                        \
+        const int s_ = (S);                                                                  \
+        const int buf = s_ & 1;                                                              \
+        if (s_ + 2 < NS) {                                                                   \
+            _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                  \
+                BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * (s_ + 2));         \
+        }                                                                                    \
+        bf16x8 Af[NA];                                                                       \
+        _Pragma("unroll") for (int x = 0; x < NA; ++x)                                       \
+            Af[x] = __builtin_bit_cast(bf16x8, As[buf][(x * 16 + r) * 4 + q]);               \
+        _Pragma("unroll") for (int t = 0; t < NTW; ++t) {                                    \
+            const bf16x8 Bf =                                                                \
+                __builtin_bit_cast(bf16x8, Bs[buf][((wave * NTW + t) * 16 + r) * 4 + q]);    \
+            _Pragma("unroll") for (int x = 0; x < NA; ++x)                                   \
+                acc[x][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[x], Bf, acc[x][t],    \
+                                                                    0, 0, 0);                \
+        }                                                                                    \
+        if (s_ + 1 < NS) {                                                                   \
+            const int g1 = (s_ + 1) >> 3;                                                    \
+            if (((s_ + 1) & 7) == 0) {                                                       \
+                stream_store(g1 & 1);                                                        \
+                if (g1 + 1 < ngroups) stream_load(g1 + 1);                                   \
+            }                                                                                \
+            regen(s_ + 1, &As[buf ^ 1][tid]);                                                \
+            _Pragma("unroll") for (int u = 0; u < NTW; ++u) Bs[buf ^ 1][tid + 512 * u] =     \
+                BSTORE[u];                                                                   \
+        }                                                                                    \
+        __syncthreads();                                                                     \
+    }
+        for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
+            SEEDMM_WIDE_STEP(s, bA, bB)
+            SEEDMM_WIDE_STEP(s + 1, bB, bA)
+        }
+#undef SEEDMM_WIDE_STEP
+
+        // ---- epilogue: D row = 16*rt + 4*q + j, column = token slot of this lane -----
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const int i = pass + (wave * NTW + t) * 16 + r;
+            if (i >= n_e) continue;
+            int64_t dst;
+            float scale = 1.0f;
+            if constexpr (MODE == MODE_GEMM) {
+                dst = i;
+            } else {
+                dst = list[i];
+                if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int m = m0 + rt * 16 + 4 * q + j;
+                    if (m >= M) continue;
+                    if constexpr (MODE == MODE_GATEUP) {
+                        const float gt = acc[rt][t][j], up = acc[RT + rt][t][j];
+                        const float hv = gt / (1.0f + expf(-gt)) * up;
+                        const __bf16 hb = (__bf16)hv;
+                        a.h[dst * a.ldy + m] = __builtin_bit_cast(uint16_t, hb);
+                    } else {
+                        a.y[dst * a.ldy + m] = scale * acc[rt][t][j];
+                    }
+                }
+            }
+        }
+        __syncthreads();   // LDS buffers are reused by the next pass
+    }
+}
+
+// ----------------------------------------------------------------------------------
 // MoE dispatch: workgroup e compacts the pairs routed to expert e, in pair order.
+// Thread t owns the contiguous run of pairs [t*R, (t+1)*R): it counts its matches, a
+// workgroup prefix sum of the counts gives its first output slot, and a second pass
+// over the run writes the pair indices.  Two round trips to memory, one barrier, no
+// atomics: the lists are deterministic.
 // ----------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_dispatch(const int32_t* __restrict__ ids, int total,
                                                   int T, int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ lists) {
     __shared__ int wsum[4];
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int base = 0;
-    int32_t* out = lists + (int64_t)e * T;
-    for (int p0 = 0; p0 < total; p0 += 256) {
-        const int p = p0 + threadIdx.x;
-        const bool hit = p < total && ids[p] == e;
-        const uint64_t bal = __ballot(hit);
-        const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
-        if (lane == 0) wsum[wave] = __popcll(bal);
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; ++w) before += wsum[w];
-        const int slot = base + before + __popcll(below);
-        if (hit && slot < T) out[slot] = p;   // ids repeated within a token: dropped
-        base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        __syncthreads();
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int R = (total + 255) / 256;
+    const int p0 = min(tid * R, total), p1 = min(p0 + R, total);
+    int c = 0;
+    for (int p = p0; p < p1; ++p) c += ids[p] == e;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
     }
-    if (threadIdx.x == 0) counts[e] = base < T ? base : T;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int slot = incl - c;
+    for (int w = 0; w < wave; ++w) slot += wsum[w];
+    int32_t* out = lists + (int64_t)e * T;
+    if (c > 0) {
+        for (int p = p0; p < p1; ++p) {
+            if (ids[p] == e) {
+                if (slot < T) out[slot] = p;   // ids repeated within a token: dropped
+                ++slot;
+            }
+        }
+    }
+    if (tid == 0) {
+        const int n = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        counts[e] = n < T ? n : T;
+    }
 }
 
 // y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.
@@ -557,9 +794,10 @@ void gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int eb, co
 // 4 row tiles, up to 256 tokens per pass.
 template <int P, bool VEC, int MODE>
 void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
-    if (prefill) {
-        dim3 grid((a.M + 63) / 64, gridy);
-        hipLaunchKernelGGL((k_mfma<P, VEC, 16, MODE, 1>), grid, dim3(256), 0, st, a);
+    if (prefill && VEC && a.K % 256 == 0) {
+        constexpr int RM = MODE == MODE_GATEUP ? 64 : 128;
+        dim3 grid((a.M + RM - 1) / RM, gridy);
+        hipLaunchKernelGGL((k_wide<P, MODE, 3>), grid, dim3(512), 0, st, a);
     } else {
         dim3 grid((a.M + 15) / 16, gridy);
         hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, 4>), grid, dim3(256), 0, st, a);
@@ -717,7 +955,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     float* obuf = (float*)(ws + L.o);
 
     auto mark = [&](int i) {
-        if (events && events[i]) hipEventRecord((hipEvent_t)events[i], st);
+        if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
     };
     mark(0);
     hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T, counts, lists);
