@@ -459,40 +459,46 @@ __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
 // ----------------------------------------------------------------------------------
 // Wide-token products (prefill and long token lists), vector-load layouts only
 // (K % 256 == 0, 16-byte aligned streams).  A workgroup of 8 waves owns AR = 128 weight
-// rows (64 rows of gate and of up, or 128 rows of one matrix) for up to NC = 8*NTW*16
-// tokens, so each weight block is regenerated once per pass over its expert's tokens.
+// rows (64 rows of gate and of up, or 128 rows of one matrix) for up to NC = 384 tokens,
+// so each weight block is regenerated once per pass over its expert's tokens.
 // Per 32-k step (blocks 4s..4s+3 of every row, contiguous k):
 //   - each thread regenerates one block and writes its 8 bf16 weights to LDS (A tile);
 //   - the step's 64-byte slice of every token row is staged in LDS (B tile);
-//   - wave w multiplies the 8 A tiles with its NTW token tiles (16x16x32 bf16 MFMA),
-//     accumulators in registers.
-// A and B are double-buffered: while the matrix cores work on step s the vector ALUs
-// regenerate step s+1 and the next B slice is in flight.  The seed / coefficient / code
-// streams of each 32-block group are staged in LDS with 16-byte loads one group ahead;
-// a row's stream chunks are written and read by the four lanes of one quad, so the
-// same-wave LDS ordering makes them visible without a barrier.
+//   - wave w = (row half rh, token quarter tq) multiplies its two 32-row A tiles (gate
+//     and up rows of one half, or two row tiles) with its three 32-token tiles on
+//     v_mfma_f32_32x32x16_bf16 (two k halves per step), accumulators in registers.
+// LDS tiles are stored per k half ([half][row or token][2 blocks][8 bf16]) so every MFMA
+// fragment is one contiguous 1 KB read.  A and B are double-buffered; the vector ALUs
+// regenerate step s+1 while the matrix cores work on step s.  Each thread's stream values
+// for step s+2 are read into registers during step s, so regeneration starts right after
+// the barrier.  The seed / coefficient / code streams of each 32-block group are staged
+// in LDS with 16-byte loads a group ahead; a row's stream chunks are written and read by
+// the four lanes of one quad (same-wave LDS order, no barrier needed).
 // Workgroups are numbered so that every row group of one expert lands on the same XCD
 // (workgroups are dealt to the 8 XCDs round-robin), keeping that expert's token rows in
 // one L2.
 // ----------------------------------------------------------------------------------
-template <int P, int MODE, int NTW>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int P, int MODE>
 __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
     constexpr int AR = 128;                   // A rows per workgroup
     constexpr int RM = AR / NMAT;             // rows per matrix
-    constexpr int RT = RM / 16;               // row tiles per matrix
-    constexpr int NA = AR / 16;               // A tiles per step
-    constexpr int NC = 8 * NTW * 16;          // token slots per pass
-    constexpr int CW = 32 * P / 4;            // coefficient words per row per group
-    __shared__ u32x4 As[2][AR * 4];
-    __shared__ u32x4 Bs[2][NC * 4];
-    __shared__ uint16_t Ss[2][AR * 32];
-    __shared__ uint16_t Cs[2][AR * CW + 8];
+    constexpr int NTW = 3;                    // 32-token tiles per wave
+    constexpr int NC = 4 * NTW * 32;          // token slots per pass (384)
+    constexpr int SROW = 40;                  // staged stream row stride in u16 (80 B: the
+                                              // 16 rows a wave reads start in distinct banks)
+    __shared__ u32x4 As[2][2 * AR * 2];
+    __shared__ u32x4 Bs[2][2 * NC * 2];
+    __shared__ uint16_t Ss[2][AR * SROW];
+    __shared__ uint16_t Cs[2][AR * SROW + 8];
     __shared__ uint8_t Ds[2][AR * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, q = lane >> 4;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int rh = wave >> 2, tq = wave & 3;
 
     // ---- XCD-aware numbering: consecutive work items share an XCD ------------------
     const int total = gridDim.x * gridDim.y;
@@ -533,6 +539,10 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     const int ngroups = nbpr / 32;            // K % 256 == 0
     const int NS = ngroups * 8;
 
+    // this wave's two A tiles (32 A-rows each): gate and up rows of half rh, or 2rh, 2rh+1
+    const int ta0 = NMAT == 2 ? rh : 2 * rh;
+    const int ta1 = NMAT == 2 ? 2 + rh : 2 * rh + 1;
+
     // ---- regeneration role: A row `arow` (matrix dmat, row drow), block lane dj ------
     const int arow = tid >> 2, dj = tid & 3;
     const int dmat = arow / RM, drow = arow % RM;
@@ -542,63 +552,74 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     }
     const bool drv = m0 + drow < M;
     const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
+    // LDS tile layout [k half][32-row group][block in half][32 rows]: a half-wave's
+    // fragment read is 512 contiguous bytes (no bank conflicts)
+    const int a_slot = ((dj >> 1) * AR + (arow & ~31)) * 2 + (dj & 1) * 32 + (arow & 31);
 
-    // stream staging: chunk dj of this row's group (seeds: 4 x 16 B, P=4 coefs 4 x 16 B,
-    // P=3 coefs 3 x 16 B, codes 1 x 16 B)
     u32x4 sreg_s, sreg_c, sreg_d;
     auto stream_load = [&](int g) {
         const int64_t b0 = drowb + 32 * g;    // first block of the group in this row
         sreg_s = *reinterpret_cast<const u32x4*>(W.seeds + b0 + 8 * dj);
         if (dj < P) sreg_c = *reinterpret_cast<const u32x4*>(W.coefs + (b0 * P) / 4 + 8 * dj);
         if (dj == 0) sreg_d = *reinterpret_cast<const u32x4*>(W.codes + b0 / 2);
-        if (!drv) sreg_c = u32x4{0u, 0u, 0u, 0u};   // missing rows decode to zero
     };
     auto stream_store = [&](int buf) {
-        *reinterpret_cast<u32x4*>(&Ss[buf][arow * 32 + 8 * dj]) = sreg_s;
-        if (dj < P) *reinterpret_cast<u32x4*>(&Cs[buf][arow * CW + 8 * dj]) = sreg_c;
+        *reinterpret_cast<u32x4*>(&Ss[buf][arow * SROW + 8 * dj]) = sreg_s;
+        // missing rows get zero coefficients (zero weights); applied here, not at the
+        // load, so the load is not waited for early
+        if (dj < P)
+            *reinterpret_cast<u32x4*>(&Cs[buf][arow * SROW + 8 * dj]) =
+                drv ? sreg_c : u32x4{0u, 0u, 0u, 0u};
         if (dj == 0) *reinterpret_cast<u32x4*>(&Ds[buf][arow * 16]) = sreg_d;
     };
-    // regenerate block (step s) of this thread from the staged streams
-    auto regen = [&](int s, u32x4* dst) {
+    struct Blk { uint32_t seed, cw, code; };
+    auto fetch = [&](int s) {
         const int buf = (s >> 3) & 1;
         const int bl = 4 * (s & 7) + dj;      // block within the group
-        const uint32_t seed = Ss[buf][arow * 32 + bl];
-        uint32_t cw;
+        Blk k;
+        k.seed = Ss[buf][arow * SROW + bl];
         if constexpr (P == 4) {
-            cw = Cs[buf][arow * CW + bl];
+            k.cw = Cs[buf][arow * SROW + bl];
         } else {
             const int n = 3 * bl, sh = 4 * (n & 3);
-            const uint16_t* c = &Cs[buf][arow * CW + (n >> 2)];
-            cw = ((uint32_t)c[0] | ((uint32_t)c[1] << 16)) >> sh;
+            const uint16_t* c = &Cs[buf][arow * SROW + (n >> 2)];
+            k.cw = ((uint32_t)c[0] | ((uint32_t)c[1] << 16)) >> sh;
         }
-        const uint32_t code = ((uint32_t)Ds[buf][arow * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
+        k.code = ((uint32_t)Ds[buf][arow * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
+        return k;
+    };
+    auto regen = [&](const Blk& k, u32x4* dst) {
         float w[8];
-        decode_block<P>(lfsr_window(seed), cw, code, W.exp_bias, w);
+        decode_block<P>(lfsr_window(k.seed), k.cw, k.code, W.exp_bias, w);
         *dst = __builtin_bit_cast(u32x4, pack_bf16(w));
     };
 
     for (int pass = 0; pass < n_e; pass += NC) {
-        // B staging role: chunks tid + 512 u = (token slot, 16-byte piece)
+        // B staging role: chunks tid + 512 u = (token slot, 16-byte piece dj)
         const uint16_t* brow[NTW];
+        int bslot[NTW];
 #pragma unroll
         for (int u = 0; u < NTW; ++u) {
-            const int i = min(pass + ((tid + 512 * u) >> 2), n_e - 1);
+            const int ts = (tid + 512 * u) >> 2;
+            const int i = min(pass + ts, n_e - 1);
             int64_t src;
             if constexpr (MODE == MODE_GEMM) src = i;
             else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
             else src = list[i];
             brow[u] = a.x + src * a.ldx + 8 * dj;
+            bslot[u] = ((dj >> 1) * NC + (ts & ~31)) * 2 + (dj & 1) * 32 + (ts & 31);
         }
 
-        f32x4 acc[NA][NTW];
+        f32x16 acc[2][NTW];
 #pragma unroll
-        for (int x = 0; x < NA; ++x)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int t = 0; t < NTW; ++t) acc[x][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NTW; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[x][t][v] = 0.f;
 
-        // prologue: streams of groups 0 (staged) and 1 (in registers), step 0 A and B in
-        // LDS, step 1 B in flight.  B slices are loaded two steps ahead of their use,
-        // alternating between two register sets (the loop is unrolled by two steps).
+        // prologue: group 0 staged, group 1 in registers; step 0's weights and B slice in
+        // buffer 0, step 1's B slice in flight, step 1's stream values in registers.
         stream_load(0);
         stream_store(0);
         if (ngroups > 1) stream_load(1);
@@ -607,41 +628,45 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
         for (int u = 0; u < NTW; ++u) bA[u] = *reinterpret_cast<const u32x4*>(brow[u]);
 #pragma unroll
         for (int u = 0; u < NTW; ++u) bB[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32);
-        regen(0, &As[0][tid]);
+        regen(fetch(0), &As[0][a_slot]);
+        Blk nxt = fetch(1);
 #pragma unroll
-        for (int u = 0; u < NTW; ++u) Bs[0][tid + 512 * u] = bA[u];
+        for (int u = 0; u < NTW; ++u) Bs[0][bslot[u]] = bA[u];
         __syncthreads();
 
-// One 32-k step s: B of step s+2 into BNEXT (free since step s's slice is in LDS),
-// MFMAs on buffer s&1, then weights and B slice (BSTORE) of step s+1 into buffer s&1^1.
+// One 32-k step s, straight-line.  The vector ALUs start at once on step s+1's weights
+// (stream values already in registers), then fetch step s+2's stream values (storing the
+// next group's streams when s+2 opens it) and issue step s+2's B loads; the matrix cores
+// work on buffer s&1 meanwhile.  Step s+1's weights and B slice (BSTORE) go to buffer
+// s&1^1.  Indices past the last step are clamped; those writes land in buffers nobody
+// reads.
 #define SEEDMM_WIDE_STEP(S, BNEXT, BSTORE)                                                   \
     {                                                                                        \
         const int s_ = (S);                                                                  \
         const int buf = s_ & 1;                                                              \
-        if (s_ + 2 < NS) {                                                                   \
-            _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                  \
-                BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * (s_ + 2));         \
+        regen(nxt, &As[buf ^ 1][a_slot]);                                                    \
+        if (((s_ + 2) & 7) == 0 && s_ + 2 < NS) {                                            \
+            const int g2 = (s_ + 2) >> 3;                                                    \
+            stream_store(g2 & 1);                                                            \
+            if (g2 + 1 < ngroups) stream_load(g2 + 1);                                       \
         }                                                                                    \
-        bf16x8 Af[NA];                                                                       \
-        _Pragma("unroll") for (int x = 0; x < NA; ++x)                                       \
-            Af[x] = __builtin_bit_cast(bf16x8, As[buf][(x * 16 + r) * 4 + q]);               \
-        _Pragma("unroll") for (int t = 0; t < NTW; ++t) {                                    \
-            const bf16x8 Bf =                                                                \
-                __builtin_bit_cast(bf16x8, Bs[buf][((wave * NTW + t) * 16 + r) * 4 + q]);    \
-            _Pragma("unroll") for (int x = 0; x < NA; ++x)                                   \
-                acc[x][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[x], Bf, acc[x][t],    \
-                                                                    0, 0, 0);                \
-        }                                                                                    \
-        if (s_ + 1 < NS) {                                                                   \
-            const int g1 = (s_ + 1) >> 3;                                                    \
-            if (((s_ + 1) & 7) == 0) {                                                       \
-                stream_store(g1 & 1);                                                        \
-                if (g1 + 1 < ngroups) stream_load(g1 + 1);                                   \
+        nxt = fetch(min(s_ + 2, NS - 1));                                                    \
+        const int snext = min(s_ + 2, NS - 1);                                               \
+        _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                      \
+            BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * snext);                \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                      \
+            const bf16x8 A0 =                                                                \
+                __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta0) * 2 + lane]);         \
+            const bf16x8 A1 =                                                                \
+                __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta1) * 2 + lane]);         \
+            _Pragma("unroll") for (int t = 0; t < NTW; ++t) {                                \
+                const bf16x8 Bf = __builtin_bit_cast(                                        \
+                    bf16x8, Bs[buf][(h * NC + 32 * (tq * NTW + t)) * 2 + lane]);             \
+                acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, Bf, acc[0][t], 0, 0, 0); \
+                acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, Bf, acc[1][t], 0, 0, 0); \
             }                                                                                \
-            regen(s_ + 1, &As[buf ^ 1][tid]);                                                \
-            _Pragma("unroll") for (int u = 0; u < NTW; ++u) Bs[buf ^ 1][tid + 512 * u] =     \
-                BSTORE[u];                                                                   \
         }                                                                                    \
+        _Pragma("unroll") for (int u = 0; u < NTW; ++u) Bs[buf ^ 1][bslot[u]] = BSTORE[u];   \
         __syncthreads();                                                                     \
     }
         for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
@@ -650,10 +675,11 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
         }
 #undef SEEDMM_WIDE_STEP
 
-        // ---- epilogue: D row = 16*rt + 4*q + j, column = token slot of this lane -----
+        // ---- epilogue: lane holds, for token slot 96 tq + 32 t + l32, rows
+        //      8 g + 4 lh + c (g, c = 0..3) of each of its two 32-row tiles -----------
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-            const int i = pass + (wave * NTW + t) * 16 + r;
+            const int i = pass + 32 * (tq * NTW + t) + l32;
             if (i >= n_e) continue;
             int64_t dst;
             float scale = 1.0f;
@@ -664,18 +690,36 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
                 if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
             }
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
+            for (int g = 0; g < 4; ++g) {
+                if constexpr (MODE == MODE_GATEUP) {
+                    const int m = m0 + 32 * rh + 8 * g + 4 * lh;
+                    uint16_t hb[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int m = m0 + rt * 16 + 4 * q + j;
-                    if (m >= M) continue;
-                    if constexpr (MODE == MODE_GATEUP) {
-                        const float gt = acc[rt][t][j], up = acc[RT + rt][t][j];
-                        const float hv = gt / (1.0f + expf(-gt)) * up;
-                        const __bf16 hb = (__bf16)hv;
-                        a.h[dst * a.ldy + m] = __builtin_bit_cast(uint16_t, hb);
+                    for (int c = 0; c < 4; ++c) {
+                        const float gt = acc[0][t][4 * g + c], up = acc[1][t][4 * g + c];
+                        hb[c] = __builtin_bit_cast(uint16_t, (__bf16)(gt / (1.0f + expf(-gt)) * up));
+                    }
+                    uint16_t* dp = a.h + dst * a.ldy + m;
+                    if (m + 3 < M && ((uintptr_t)dp & 7) == 0) {
+                        *reinterpret_cast<uint2*>(dp) =
+                            make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
                     } else {
-                        a.y[dst * a.ldy + m] = scale * acc[rt][t][j];
+                        for (int c = 0; c < 4; ++c)
+                            if (m + c < M) dp[c] = hb[c];
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        const int m = m0 + 32 * (x == 0 ? ta0 : ta1) + 8 * g + 4 * lh;
+                        float* dp = a.y + dst * a.ldy + m;
+                        const f32x4 v = {scale * acc[x][t][4 * g + 0], scale * acc[x][t][4 * g + 1],
+                                         scale * acc[x][t][4 * g + 2], scale * acc[x][t][4 * g + 3]};
+                        if (m + 3 < M && ((uintptr_t)dp & 15) == 0) {
+                            *reinterpret_cast<f32x4*>(dp) = v;
+                        } else {
+                            for (int c = 0; c < 4; ++c)
+                                if (m + c < M) dp[c] = v[c];
+                        }
                     }
                 }
             }
@@ -797,7 +841,7 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     if (prefill && VEC && a.K % 256 == 0) {
         constexpr int RM = MODE == MODE_GATEUP ? 64 : 128;
         dim3 grid((a.M + RM - 1) / RM, gridy);
-        hipLaunchKernelGGL((k_wide<P, MODE, 3>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((k_wide<P, MODE>), grid, dim3(512), 0, st, a);
     } else {
         dim3 grid((a.M + 15) / 16, gridy);
         hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, 4>), grid, dim3(256), 0, st, a);
