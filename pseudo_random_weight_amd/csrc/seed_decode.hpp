@@ -58,9 +58,26 @@ __device__ __forceinline__ Window window_from_next32(uint32_t seed16, uint32_t n
     return w;
 }
 
+// Window from two 256-entry tables of 32-bit continuations: the continuation is
+// GF(2)-linear in the seed, so next32(seed) = lo[seed & 0xFF] ^ hi[seed >> 8] with
+// lo[b] = next32(b) and hi[b] = next32(b << 8).  `tab` holds lo in [0, 256) and hi in
+// [256, 512) (LDS).
+__device__ __forceinline__ Window window_from_tables(uint32_t seed16, const uint32_t* tab) {
+    const uint32_t n32 = tab[seed16 & 0xFFu] ^ tab[256 + (seed16 >> 8)];
+    return window_from_next32(seed16, n32);
+}
+
 // 32-bit continuation x_16..x_47 of a seed (used to fill the lookup tables).
 __device__ __forceinline__ uint32_t lfsr_next32(uint32_t seed16) {
     return lfsr_window(seed16).lo;
+}
+
+// Fills the two continuation tables (512 words of LDS) with the workgroup's threads and
+// waits for them; call before any thread of the workgroup can leave.
+__device__ __forceinline__ void fill_lfsr_tables(uint32_t* tab) {
+    for (int i = threadIdx.x; i < 512; i += blockDim.x)
+        tab[i] = lfsr_next32(i < 256 ? (uint32_t)i : (uint32_t)(i - 256) << 8);
+    __syncthreads();
 }
 
 // State s_t (1 <= t <= 32) of a window.  Callers unroll their loops, so t folds to a

@@ -179,6 +179,8 @@ __global__ __launch_bounds__(256) void k_gemv_f32(const uint16_t* __restrict__ s
                                                   int ldx, float* __restrict__ y, int ldy,
                                                   int M, int K, int N) {
     __shared__ float red[4][NTOK][16];
+    __shared__ uint32_t tab[512];
+    fill_lfsr_tables(tab);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
     const int row = blockIdx.x * 16 + r;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(256) void k_gemv_f32(const uint16_t* __restrict__ s
         for (int s = 0; s < 8; ++s) {
             if (!VEC && s >= nvalid) break;
             const int kb = g * 8 + s;
-            const Window win = lfsr_window(sg.seed(s));
+            const Window win = window_from_tables(sg.seed(s), tab);
             int f[8];
             block_sums<P>(win, sg.coef(s), f);
             const float sc = block_scale(sg.code(s), exp_bias);
@@ -271,6 +273,7 @@ struct MfmaArgs {
 
 // Per-lane state of one pass over K.
 struct Lane {
+    const uint32_t* tab;  // LDS continuation tables (TAB kernels), else null
     Mat W1, W2;
     int64_t rowb;        // first block of this lane's row (row clamped into range)
     bool rv;             // the row exists
@@ -279,7 +282,13 @@ struct Lane {
 
 // One pass over K for NTA token tiles.  Branch-free: addresses are clamped into range
 // and padding blocks get all-zero coefficients, which decode to exact zero weights.
-template <int P, bool VEC, int NMAT, int NTA, int KSPLIT>
+template <bool TAB>
+__device__ __forceinline__ Window window_of(uint32_t seed16, const uint32_t* tab) {
+    if constexpr (TAB) return window_from_tables(seed16, tab);
+    else return lfsr_window(seed16);
+}
+
+template <int P, bool VEC, int NMAT, int NTA, int KSPLIT, bool TAB>
 __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const* brow,
                                             f32x4* acc, f32x4* acc2) {
     constexpr int GSTRIDE = KSPLIT * 4;
@@ -297,12 +306,12 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
             const bool bv = s < nvalid;
             const int kb = min(gc * 8 + s, L.nbpr - 1);
             float w[8];
-            decode_block<P>(lfsr_window(s1.seed(s)), bv ? s1.coef(s) : 0u, s1.code(s),
+            decode_block<P>(window_of<TAB>(s1.seed(s), L.tab), bv ? s1.coef(s) : 0u, s1.code(s),
                             L.W1.exp_bias, w);
             const bf16x8 A = pack_bf16(w);
             bf16x8 A2;
             if constexpr (NMAT == 2) {
-                decode_block<P>(lfsr_window(s2.seed(s)), bv ? s2.coef(s) : 0u, s2.code(s),
+                decode_block<P>(window_of<TAB>(s2.seed(s), L.tab), bv ? s2.coef(s) : 0u, s2.code(s),
                                 L.W2.exp_bias, w);
                 A2 = pack_bf16(w);
             }
@@ -318,7 +327,7 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
 }
 
 // One pass: NTA tiles of 16 tokens starting at token slot `pass`.
-template <int P, bool VEC, int NTA, int MODE, int KSPLIT, int NT>
+template <int P, bool VEC, int NTA, int MODE, int KSPLIT, int NT, bool TAB>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, const int32_t* list,
                                           int n_e, int pass, int m0, int lane, int r,
                                           f32x4 (*red)[NT * (MODE == MODE_GATEUP ? 2 : 1)][64]) {
@@ -341,7 +350,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    mfma_k_loop<P, VEC, NMAT, NTA, KSPLIT>(L, brow, acc, acc2);
+    mfma_k_loop<P, VEC, NMAT, NTA, KSPLIT, TAB>(L, brow, acc, acc2);
 
     if constexpr (KSPLIT > 1) {
 #pragma unroll
@@ -393,11 +402,13 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
     if constexpr (KSPLIT > 1) __syncthreads();
 }
 
-template <int P, bool VEC, int NT, int MODE, int KSPLIT>
+template <int P, bool VEC, int NT, int MODE, int KSPLIT, bool TAB>
 __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
     constexpr int ROWT = 4 / KSPLIT;
     constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
     __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][NT * NMAT][64];
+    __shared__ uint32_t tab[TAB ? 512 : 1];
+    if constexpr (TAB) fill_lfsr_tables(tab);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15;
@@ -429,6 +440,7 @@ __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
     if (n_e <= 0) return;
 
     Lane L;
+    L.tab = TAB ? tab : nullptr;
     L.ks = wave % KSPLIT;
     L.q = lane >> 4;
     const int rt = wave / KSPLIT;
@@ -448,10 +460,10 @@ __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
         const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
         static_assert(NT == 4, "the decode kernel holds at most 4 token tiles");
         switch (ntiles) {
-            case 1: mfma_pass<P, VEC, 1, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            case 2: mfma_pass<P, VEC, 2, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            case 3: mfma_pass<P, VEC, 3, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            default: mfma_pass<P, VEC, 4, MODE, KSPLIT, NT>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            case 1: mfma_pass<P, VEC, 1, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            case 2: mfma_pass<P, VEC, 2, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            case 3: mfma_pass<P, VEC, 3, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            default: mfma_pass<P, VEC, 4, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
         }
     }
 }
@@ -494,6 +506,8 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     __shared__ uint16_t Ss[2][AR * SROW];
     __shared__ uint16_t Cs[2][AR * SROW + 8];
     __shared__ uint8_t Ds[2][AR * 16];
+    __shared__ uint32_t tab[512];
+    fill_lfsr_tables(tab);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -590,7 +604,7 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     };
     auto regen = [&](const Blk& k, u32x4* dst) {
         float w[8];
-        decode_block<P>(lfsr_window(k.seed), k.cw, k.code, W.exp_bias, w);
+        decode_block<P>(window_from_tables(k.seed, tab), k.cw, k.code, W.exp_bias, w);
         *dst = __builtin_bit_cast(u32x4, pack_bf16(w));
     };
 
@@ -844,7 +858,7 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
         hipLaunchKernelGGL((k_wide<P, MODE>), grid, dim3(512), 0, st, a);
     } else {
         dim3 grid((a.M + 15) / 16, gridy);
-        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, 4>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, 4, true>), grid, dim3(256), 0, st, a);
     }
 }
 
