@@ -250,9 +250,9 @@ __global__ __launch_bounds__(256) void k_gemv_f32(const uint16_t* __restrict__ s
 //   MODE_GEMM   : y[n][m] = sum_k W[m][k] x[n][k]                       (one matrix)
 //   MODE_GATEUP : h[p][m] = bf16( silu(G_e x_t)[m] * (U_e x_t)[m] ),  t = p / top_k
 //   MODE_DOWN   : o[p][m] = w[p] * (D_e h_p)[m]
-// Grid: x = row tiles (16 * ROWT rows), y = active experts (expert y = the y-th expert
-// with a nonzero count).  KSPLIT waves split K (then ROWT = 1) or ROWT = 4 waves own
-// different rows (KSPLIT = 1).  Tokens are processed in passes of NT*16.
+// Grid: x = tiles of 16 weight rows, y = active experts (expert y = the y-th expert with
+// a nonzero count).  The 4 waves of a workgroup split K (and, for GATEUP, the two
+// matrices).  Tokens are processed in passes of NT*16.
 // ----------------------------------------------------------------------------------
 struct MfmaArgs {
     seedmm_mat A;           // gate (GATEUP) or the matrix
@@ -274,64 +274,66 @@ struct MfmaArgs {
 // Per-lane state of one pass over K.
 struct Lane {
     const uint32_t* tab;  // LDS continuation tables (TAB kernels), else null
-    Mat W1, W2;
+    Mat W;               // the matrix this wave regenerates
     int64_t rowb;        // first block of this lane's row (row clamped into range)
     bool rv;             // the row exists
     int nbpr, nseg, n_it, ks, q;
 };
 
-// One pass over K for NTA token tiles.  Branch-free: addresses are clamped into range
-// and padding blocks get all-zero coefficients, which decode to exact zero weights.
 template <bool TAB>
 __device__ __forceinline__ Window window_of(uint32_t seed16, const uint32_t* tab) {
     if constexpr (TAB) return window_from_tables(seed16, tab);
     else return lfsr_window(seed16);
 }
 
-template <int P, bool VEC, int NMAT, int NTA, int KSPLIT, bool TAB>
+// One pass over this wave's share of K for NTA token tiles.  Branch-free: addresses are
+// clamped into range and padding blocks get all-zero coefficients, which decode to exact
+// zero weights.  The stream words of the next segment are loaded while the current one
+// is regenerated.
+template <int P, bool VEC, int NTA, int KS, bool TAB>
 __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const* brow,
-                                            f32x4* acc, f32x4* acc2) {
-    constexpr int GSTRIDE = KSPLIT * 4;
-    for (int it = 0; it < L.n_it; ++it) {
+                                            f32x4* acc) {
+    constexpr int GSTRIDE = KS * 4;
+    auto seg = [&](int it, int& gc, int& nvalid) {
         const int g = it * GSTRIDE + L.ks * 4 + L.q;
-        const bool gv = g < L.nseg && L.rv;
-        const int gc = g < L.nseg ? g : L.nseg - 1;
-        const int nvalid = gv ? min(8, L.nbpr - gc * 8) : 0;
-        Seg<P, VEC> s1, s2;
-        s1.load(L.W1.seeds, L.W1.coefs, L.W1.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
-        if constexpr (NMAT == 2)
-            s2.load(L.W2.seeds, L.W2.coefs, L.W2.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
+        gc = g < L.nseg ? g : L.nseg - 1;
+        nvalid = (g < L.nseg && L.rv) ? min(8, L.nbpr - gc * 8) : 0;
+    };
+    int gc, nvalid;
+    seg(0, gc, nvalid);
+    Seg<P, VEC> cur;
+    cur.load(L.W.seeds, L.W.coefs, L.W.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
+    for (int it = 0; it < L.n_it; ++it) {
+        int gn, nvn;
+        seg(it + 1 < L.n_it ? it + 1 : it, gn, nvn);
+        Seg<P, VEC> nxt;
+        nxt.load(L.W.seeds, L.W.coefs, L.W.codes, L.rowb + gn * 8, VEC ? 8 : nvn);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const bool bv = s < nvalid;
             const int kb = min(gc * 8 + s, L.nbpr - 1);
             float w[8];
-            decode_block<P>(window_of<TAB>(s1.seed(s), L.tab), bv ? s1.coef(s) : 0u, s1.code(s),
-                            L.W1.exp_bias, w);
+            decode_block<P>(window_of<TAB>(cur.seed(s), L.tab), bv ? cur.coef(s) : 0u,
+                            cur.code(s), L.W.exp_bias, w);
             const bf16x8 A = pack_bf16(w);
-            bf16x8 A2;
-            if constexpr (NMAT == 2) {
-                decode_block<P>(window_of<TAB>(s2.seed(s), L.tab), bv ? s2.coef(s) : 0u, s2.code(s),
-                                L.W2.exp_bias, w);
-                A2 = pack_bf16(w);
-            }
 #pragma unroll
             for (int t = 0; t < NTA; ++t) {
                 const bf16x8 B = load_bf16x8(brow[t] + 8 * kb);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
-                if constexpr (NMAT == 2)
-                    acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc2[t], 0, 0, 0);
             }
         }
+        cur = nxt;
+        gc = gn;
+        nvalid = nvn;
     }
 }
 
 // One pass: NTA tiles of 16 tokens starting at token slot `pass`.
-template <int P, bool VEC, int NTA, int MODE, int KSPLIT, int NT, bool TAB>
+template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, const int32_t* list,
-                                          int n_e, int pass, int m0, int lane, int r,
-                                          f32x4 (*red)[NT * (MODE == MODE_GATEUP ? 2 : 1)][64]) {
-    constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
+                                          int n_e, int pass, int m0, int wave, int lane, int r,
+                                          f32x4 (*red)[NT][64]) {
+    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4;   // waves sharing one matrix's K range
     // B rows of this lane (token column r of every tile); slots past n_e repeat the last
     // token so every load stays in range -- their outputs are never stored.
     const uint16_t* brow[NTA];
@@ -344,35 +346,24 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
         else src = list[i];
         brow[t] = a.x + src * a.ldx;
     }
-    f32x4 acc[NTA], acc2[NTA];
+    f32x4 acc[NTA];
 #pragma unroll
-    for (int t = 0; t < NTA; ++t) {
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    mfma_k_loop<P, VEC, NMAT, NTA, KSPLIT, TAB>(L, brow, acc, acc2);
+    for (int t = 0; t < NTA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_k_loop<P, VEC, NTA, KS, TAB>(L, brow, acc);
 
-    if constexpr (KSPLIT > 1) {
+    // partial sums of the four waves meet in LDS; wave t % 4 finishes tile t
 #pragma unroll
-        for (int t = 0; t < NTA; ++t) {
-            red[L.ks][t][lane] = acc[t];
-            if constexpr (NMAT == 2) red[L.ks][NT + t][lane] = acc2[t];
-        }
-        __syncthreads();
-    }
+    for (int t = 0; t < NTA; ++t) red[wave][t][lane] = acc[t];
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < NTA; ++t) {
-        if (KSPLIT > 1 && (t % KSPLIT) != L.ks) continue;
-        f32x4 v = acc[t], v2 = acc2[t];
-        if constexpr (KSPLIT > 1) {
-            v = red[0][t][lane];
-#pragma unroll
-            for (int w = 1; w < KSPLIT; ++w) v += red[w][t][lane];
-            if constexpr (NMAT == 2) {
-                v2 = red[0][NT + t][lane];
-#pragma unroll
-                for (int w = 1; w < KSPLIT; ++w) v2 += red[w][NT + t][lane];
-            }
+        if ((t & 3) != wave) continue;
+        f32x4 v, v2;
+        if constexpr (MODE == MODE_GATEUP) {
+            v = red[0][t][lane] + red[1][t][lane];      // gate
+            v2 = red[2][t][lane] + red[3][t][lane];     // up
+        } else {
+            v = ((red[0][t][lane] + red[1][t][lane]) + red[2][t][lane]) + red[3][t][lane];
         }
         const int i = pass + 16 * t + r;     // D column = token slot
         if (i >= n_e) continue;
@@ -399,14 +390,15 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
             }
         }
     }
-    if constexpr (KSPLIT > 1) __syncthreads();
+    __syncthreads();
 }
 
-template <int P, bool VEC, int NT, int MODE, int KSPLIT, bool TAB>
-__global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
-    constexpr int ROWT = 4 / KSPLIT;
-    constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
-    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][NT * NMAT][64];
+// 4 waves on 16 weight rows.  GATEUP: waves 0-1 regenerate gate, waves 2-3 up, each
+// over half of K; otherwise the 4 waves take a quarter of K each.
+template <int P, bool VEC, int NT, int MODE, bool TAB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2))) void k_mfma(const MfmaArgs a) {
+    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4;
+    __shared__ f32x4 red[4][NT][64];
     __shared__ uint32_t tab[TAB ? 512 : 1];
     if constexpr (TAB) fill_lfsr_tables(tab);
 
@@ -441,29 +433,27 @@ __global__ __launch_bounds__(256) void k_mfma(const MfmaArgs a) {
 
     Lane L;
     L.tab = TAB ? tab : nullptr;
-    L.ks = wave % KSPLIT;
+    L.ks = wave % KS;
     L.q = lane >> 4;
-    const int rt = wave / KSPLIT;
     L.nbpr = a.K / 8;
     const int64_t nblk = (int64_t)a.M * L.nbpr;
-    L.W1 = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
-    L.W2 = L.W1;
-    if constexpr (MODE == MODE_GATEUP) L.W2 = mat_of(a.A2, e, nblk, P, 0, true);
-    const int m0 = (blockIdx.x * ROWT + rt) * 16;
+    if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true);
+    else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
+    const int m0 = blockIdx.x * 16;
     const int row = m0 + r;
     L.rv = row < a.M;
     L.rowb = (int64_t)(L.rv ? row : a.M - 1) * L.nbpr;
     L.nseg = (L.nbpr + 7) / 8;
-    L.n_it = (L.nseg + KSPLIT * 4 - 1) / (KSPLIT * 4);
+    L.n_it = (L.nseg + KS * 4 - 1) / (KS * 4);
 
     for (int pass = 0; pass < n_e; pass += NT * 16) {
         const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
         static_assert(NT == 4, "the decode kernel holds at most 4 token tiles");
         switch (ntiles) {
-            case 1: mfma_pass<P, VEC, 1, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            case 2: mfma_pass<P, VEC, 2, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            case 3: mfma_pass<P, VEC, 3, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
-            default: mfma_pass<P, VEC, 4, MODE, KSPLIT, NT, TAB>(a, L, list, n_e, pass, m0, lane, r, red); break;
+            case 1: mfma_pass<P, VEC, 1, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            case 2: mfma_pass<P, VEC, 2, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            case 3: mfma_pass<P, VEC, 3, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            default: mfma_pass<P, VEC, 4, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
         }
     }
 }
@@ -858,7 +848,7 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
         hipLaunchKernelGGL((k_wide<P, MODE>), grid, dim3(512), 0, st, a);
     } else {
         dim3 grid((a.M + 15) / 16, gridy);
-        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, 4, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, true>), grid, dim3(256), 0, st, a);
     }
 }
 

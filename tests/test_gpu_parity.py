@@ -155,6 +155,24 @@ def test_gemv_ex_bf16_matches_oracle(sm, oracle, P, N):
     assert rel_l2(y, ref_b) <= 1e-5
 
 
+@pytest.mark.parametrize("P", [4, 3])
+@pytest.mark.parametrize("M,K", SHAPES + [(40, 1032), (24, 2056)])
+def test_gemv_ex_bf16_shapes(sm, oracle, P, M, K):
+    """bf16 products over ragged shapes: the per-block path with several K iterations
+    per wave (K % 64 != 0 and more than 16 segments) and the vector path's tails."""
+    import torch
+    say("gemv_ex bf16 shape", M, K, P)
+    base = synth.config_seed(1)
+    mat = synth.seed_matrix(base, f"gs{P}.{M}.{K}", M, K, P)
+    xt, x32 = bf16_tensor(synth.normal_f32(base, f"xs{M}.{K}", (5, K)))
+    y = sm.gemv_ex(dev(mat), xt, M, K, P)
+    torch.cuda.synchronize()
+    Wb = synth.bf16_bits_to_f32(oracle.reconstruct_bf16(mat, M, K, P)).astype(np.float64)
+    ref_b = x32.astype(np.float64) @ Wb.T
+    assert rel_l2(y.cpu().numpy(), ref_b) <= 1e-5
+    assert rel_l2(y.cpu().numpy(), oracle.gemv(mat, x32, M, K, P)) <= 1e-2
+
+
 def test_dispatch_groups_pairs_in_order(sm):
     import torch
     for (T, E, k) in [(1, 100, 8), (64, 100, 8), (37, 5, 3), (4096, 100, 8), (3, 16, 1)]:
@@ -278,6 +296,18 @@ def test_moe_edge_cases(sm, oracle):
                 torch.zeros((0, H), dtype=torch.bfloat16, device="cuda"), E, H, I, P,
                 dev(gate), dev(up), dev(down))
     assert yt.shape == (0, H)
+
+
+@pytest.mark.parametrize("P", [4, 3])
+def test_moe_per_block_path_long_rows(sm, oracle, P):
+    """H, I not multiples of 64 and long enough that every wave loops over several K
+    segments (per-block stream loads with the next segment prefetched)."""
+    E, H, I, T, k = 4, 1032, 264, 6, 2
+    say("moe per-block long rows", P)
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 7, f"long{P}")
+    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
+    assert rel_l2(y, ref) <= 1e-2
 
 
 def test_moe_is_deterministic_and_permutation_equivariant(sm):
