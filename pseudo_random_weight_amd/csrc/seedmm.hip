@@ -503,6 +503,7 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, lh = lane >> 5;
     const int rh = wave >> 2, tq = wave & 3;
+    const bool vfirst = __builtin_amdgcn_readfirstlane(rh) == 0;   // wave-uniform
 
     // ---- XCD-aware numbering: consecutive work items share an XCD ------------------
     const int total = gridDim.x * gridDim.y;
@@ -644,11 +645,10 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
 // work on buffer s&1 meanwhile.  Step s+1's weights and B slice (BSTORE) go to buffer
 // s&1^1.  Indices past the last step are clamped; those writes land in buffers nobody
 // reads.
-#define SEEDMM_WIDE_STEP(S, BNEXT, BSTORE)                                                   \
+#define SEEDMM_WIDE_REGEN(S, BNEXT)                                                          \
     {                                                                                        \
         const int s_ = (S);                                                                  \
-        const int buf = s_ & 1;                                                              \
-        regen(nxt, &As[buf ^ 1][a_slot]);                                                    \
+        regen(nxt, &As[(s_ & 1) ^ 1][a_slot]);                                               \
         if (((s_ + 2) & 7) == 0 && s_ + 2 < NS) {                                            \
             const int g2 = (s_ + 2) >> 3;                                                    \
             stream_store(g2 & 1);                                                            \
@@ -658,6 +658,10 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
         const int snext = min(s_ + 2, NS - 1);                                               \
         _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                      \
             BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * snext);                \
+    }
+#define SEEDMM_WIDE_MFMA(S)                                                                  \
+    {                                                                                        \
+        const int buf = (S) & 1;                                                             \
         _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                      \
             const bf16x8 A0 =                                                                \
                 __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta0) * 2 + lane]);         \
@@ -670,14 +674,32 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
                 acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, Bf, acc[1][t], 0, 0, 0); \
             }                                                                                \
         }                                                                                    \
-        _Pragma("unroll") for (int u = 0; u < NTW; ++u) Bs[buf ^ 1][bslot[u]] = BSTORE[u];   \
+    }
+// Waves 0-3 regenerate first and multiply second, waves 4-7 the other way round, so the
+// two waves sharing a SIMD keep its vector ALU and its matrix core busy at the same time.
+#define SEEDMM_WIDE_STEP(S, BNEXT, BSTORE, FIRST, SECOND)                                    \
+    {                                                                                        \
+        FIRST;                                                                               \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        SECOND;                                                                              \
+        _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                      \
+            Bs[((S) & 1) ^ 1][bslot[u]] = BSTORE[u];                                         \
         __syncthreads();                                                                     \
     }
-        for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
-            SEEDMM_WIDE_STEP(s, bA, bB)
-            SEEDMM_WIDE_STEP(s + 1, bB, bA)
+        if (vfirst) {
+            for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
+                SEEDMM_WIDE_STEP(s, bA, bB, SEEDMM_WIDE_REGEN(s, bA), SEEDMM_WIDE_MFMA(s))
+                SEEDMM_WIDE_STEP(s + 1, bB, bA, SEEDMM_WIDE_REGEN(s + 1, bB), SEEDMM_WIDE_MFMA(s + 1))
+            }
+        } else {
+            for (int s = 0; s < NS; s += 2) {
+                SEEDMM_WIDE_STEP(s, bA, bB, SEEDMM_WIDE_MFMA(s), SEEDMM_WIDE_REGEN(s, bA))
+                SEEDMM_WIDE_STEP(s + 1, bB, bA, SEEDMM_WIDE_MFMA(s + 1), SEEDMM_WIDE_REGEN(s + 1, bB))
+            }
         }
 #undef SEEDMM_WIDE_STEP
+#undef SEEDMM_WIDE_MFMA
+#undef SEEDMM_WIDE_REGEN
 
         // ---- epilogue: lane holds, for token slot 96 tq + 32 t + l32, rows
         //      8 g + 4 lh + c (g, c = 0..3) of each of its two 32-row tiles -----------
