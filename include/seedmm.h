@@ -127,11 +127,15 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
  *     e = topk_ids[t][s],  silu(z) = z / (1 + exp(-z)).
  *   x: bf16 [T][H] (raw bits), y: fp32 [T][H] (overwritten);
  *   gate, up: E stacked [I][H] matrices; down: E stacked [H][I] matrices;
+ *   topk_ids: int32[T][top_k], each in [0, E) and distinct within a token (the caller
+ *   validates them; a token that breaks this gets undefined y);
  *   workspace: device scratch of at least seedmm_moe_workspace_bytes(T, top_k, E, H, I)
- *   bytes, 256-byte aligned; its contents need not be initialised.
+ *   bytes, 16-byte aligned; its contents need not be initialised.  Calls that overlap
+ *   in time must use different workspaces.
  *   Expert products run on the matrix cores with bf16 weights and fp32 accumulation;
  *   the SwiGLU output is rounded to bf16 before the down product; the slots of a token
- *   are summed in slot order, so results are bit-reproducible.
+ *   are summed in slot order, so results are bit-reproducible and a token's output does
+ *   not depend on the other tokens of the batch.
  * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], E < 1 or
  * > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
  * SEEDMM_EALIGN (x not 16-byte aligned or H % 8 != 0), SEEDMM_EWORKSPACE, SEEDMM_EHIP.

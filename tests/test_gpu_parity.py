@@ -243,7 +243,7 @@ def test_moe_layer_full(sm, oracle, P, T):
     assert rel_l2(y, ref) <= 1e-2
 
 
-@pytest.mark.parametrize("P,T", [(4, 16), (4, 64), (3, 16)])
+@pytest.mark.parametrize("P,T", [(4, 16), (4, 64), (3, 16), (4, 160)])
 def test_moe_layer_sampled_tokens(sm, oracle, P, T):
     say("moe sampled", P, T)
     E, H, I, k = 100, 2048, 1024, 8
@@ -252,6 +252,17 @@ def test_moe_layer_sampled_tokens(sm, oracle, P, T):
     for t in (0, T // 2, T - 1):
         ref = oracle.moe(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, P, gate, up, down)
         assert rel_l2(y[t], ref[0]) <= 1e-2, t
+
+
+def test_moe_output_independent_of_batch(sm):
+    """A token's output bits do not depend on the other tokens of its batch (128 vs 129
+    tokens: different tile fill and expert lists)."""
+    E, H, I, P, k = 100, 2048, 1024, 4, 8
+    say("moe batch independence 128 vs 129 tokens")
+    gate, up, down, ids, w, x = moe_case(129, E, H, I, P, k, 2, "paths")
+    y_big, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)        # 1032 pairs
+    y_small, _ = run_moe(sm, gate, up, down, ids[:128], w[:128], x[:128], E, H, I, P)
+    assert np.array_equal(y_small.view(np.uint32), y_big[:128].view(np.uint32))
 
 
 def test_moe_prefill_path_small(sm, oracle):
