@@ -99,6 +99,14 @@ struct Seg {
         if constexpr (VEC) return __builtin_amdgcn_ubfe(cd, 4 * s, 4);
         else return d1[s];
     }
+    // VEC: all-zero coefficients for a segment outside the matrix (zero weights); the
+    // per-block path loads zeros for missing blocks already
+    __device__ __forceinline__ void clear_coefs_unless(bool keep) {
+        if constexpr (VEC) {
+#pragma unroll
+            for (int k = 0; k < (P == 4 ? 4 : 3); ++k) cf[k] = keep ? cf[k] : 0u;
+        }
+    }
 };
 
 // Base pointers of matrix `e` of E stacked [M][K] matrices.
@@ -308,14 +316,16 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
         seg(it + 1 < L.n_it ? it + 1 : it, gn, nvn);
         Seg<P, VEC> nxt;
         nxt.load(L.W.seeds, L.W.coefs, L.W.codes, L.rowb + gn * 8, VEC ? 8 : nvn);
+        cur.clear_coefs_unless(nvalid > 0);   // VEC segments are whole or absent
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const bool bv = s < nvalid;
-            const int kb = min(gc * 8 + s, L.nbpr - 1);
             float w[8];
-            decode_block<P>(window_of<TAB>(cur.seed(s), L.tab), bv ? cur.coef(s) : 0u,
-                            cur.code(s), L.W.exp_bias, w);
+            decode_block<P>(window_of<TAB>(cur.seed(s), L.tab), cur.coef(s), cur.code(s),
+                            L.W.exp_bias, w);
             const bf16x8 A = pack_bf16(w);
+            // VEC rows hold whole segments, so block gc*8+s exists; the per-block path
+            // clamps the padding blocks of a row's last segment
+            const int kb = VEC ? gc * 8 + s : min(gc * 8 + s, L.nbpr - 1);
 #pragma unroll
             for (int t = 0; t < NTA; ++t) {
                 const bf16x8 B = load_bf16x8(brow[t] + 8 * kb);
