@@ -5,13 +5,18 @@ A step is one decode pass of a routed mixture-of-experts layer whose expert weig
 are SeedLM seeds: 100 SwiGLU experts 2048 -> 1024 -> 2048, P = 4, top-8 softmax
 routing, T bf16 tokens (default 64): dispatch, fused gate/up + SwiGLU, down, ordered
 combine.  Inputs are synthetic (seeded generator), resident in HBM before timing;
-routing and activations are fresh every step and the weights rotate over replicas so
-every step reads its compressed weights from HBM, not from the 256 MB Infinity Cache.
+the weights rotate over replicas so every step reads its compressed weights from HBM,
+not from the 256 MB Infinity Cache.
+
+Two timed regions: eager launches with HIP events between the kernels (fresh routing
+and activations every step) give the per-stage times and the roofline of the dominant
+kernel (fused gate/up); HIP-graph replays of the whole layer call (six captured input
+sets, each with its own routing and activations) give the step time, as a serving loop
+that captures its decode step would run it (--eager times the eager launches instead).
 
 Prints one JSON line: effective weights/s (distinct expert weights applied per second),
-compressed HBM GB/s and its fraction of 8 TB/s, decode tokens/s, the roofline of the
-dominant kernel (fused gate/up) from HIP events inside the timed region, and the CPU
-oracle timed on a bounded sample of the same step.
+compressed HBM GB/s and its fraction of 8 TB/s, decode tokens/s, the roofline, and the
+CPU oracle timed on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -45,6 +50,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the T = 1, 4, 16 lines")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     return ap.parse_args()
 
 
@@ -194,7 +201,53 @@ def main():
         distinct = [len(np.unique(ids_h[warmup + s])) for s in range(steps)]
         return wall / steps, stages, np.array(distinct, dtype=np.float64), ids_h, x_d, w_d
 
-    t_step, stages, distinct, ids_h, x_d, w_d = run(T, args.warmup, args.steps)
+    NB = 6   # input sets cycled by the graph replays (each paired with replica g % replicas)
+
+    def run_graph(T, warmup, steps):
+        """Per-step time of HIP-graph replays: one graph per input set captures the whole
+        layer call (dispatch, gate/up, down, combine), as a serving loop would."""
+        ids_d, w_d, x_d, ids_h = make_batches(T, NB)
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(seedmm.moe_workspace_bytes(T, TOPK, E, H, I), dtype=torch.uint8,
+                         device=dev)
+
+        def call(g):
+            r = reps[g % len(reps)]
+            seedmm.moe(ids_d[g], w_d[g], x_d[g], E, H, I, P, r["gate"], r["up"], r["down"],
+                       y=y, workspace=ws)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for g in range(NB):
+                call(g)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for g in range(NB):
+            G = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(G):
+                call(g)
+            graphs.append(G)
+        for s_ in range(warmup):
+            graphs[s_ % NB].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            graphs[s_ % NB].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        distinct = np.array([len(np.unique(ids_h[s_ % NB])) for s_ in range(steps)], dtype=np.float64)
+        del graphs
+        return wall / steps, distinct
+
+    # stage times and the roofline come from eager launches with HIP events around each
+    # kernel; the step time is HIP-graph replays unless --eager
+    t_eager, stages, distinct, ids_h, x_d, w_d = run(T, args.warmup, args.steps)
+    if args.eager:
+        t_step = t_eager
+    else:
+        t_step, distinct = run_graph(T, args.warmup, args.steps)
     w_per_mat = H * I
     weights = distinct.mean() * 3 * w_per_mat
     cbytes = distinct.mean() * 3 * compressed_bytes_per_matrix(P)
@@ -228,6 +281,9 @@ def main():
         "distinct_experts_per_step": distinct.mean(),
         "stage_us": {"dispatch": stages[0] * 1e6, "gate_up": stages[1] * 1e6,
                      "down": stages[2] * 1e6, "combine": stages[3] * 1e6},
+        "step_timing": "eager launches" if args.eager else
+                       f"HIP-graph replays of the layer call ({NB} captured input sets)",
+        "ms_per_step_eager": t_eager * 1e3,
         "roofline": roofline,
     }
 
@@ -237,6 +293,8 @@ def main():
             if Ts == T:
                 continue
             ts, st, dis, *_ = run(Ts, 3, 20)
+            if not args.eager:
+                ts, dis = run_graph(Ts, 3, 50)
             sweep[str(Ts)] = {"ms_per_step": ts * 1e3, "tok_s": Ts / ts,
                               "weights_per_s": dis.mean() * 3 * w_per_mat / ts,
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,

@@ -265,6 +265,40 @@ def test_moe_output_independent_of_batch(sm):
     assert np.array_equal(y_small.view(np.uint32), y_big[:128].view(np.uint32))
 
 
+def test_moe_graph_replays_match_eager(sm):
+    """The layer call captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, gives the eager result bit for bit."""
+    import torch
+    E, H, I, P, k, T = 100, 2048, 1024, 4, 8, 4
+    say("moe graph replay")
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2, "graph")
+    y_ref, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    g, u, d = dev(gate), dev(up), dev(down)
+    ids_t, w_t = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    xt, _ = bf16_tensor(x)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sm.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    G = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(G):
+        sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, y=y, workspace=ws)
+    other = torch.from_numpy(np.roll(ids, 1, axis=0)).cuda()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0xFF)
+        G.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), rep
+        # eager work between replays, on the same workspace
+        sm.moe(other, w_t, xt, E, H, I, P, g, u, d, y=torch.empty_like(y), workspace=ws)
+        torch.cuda.synchronize()
+
+
 def test_moe_prefill_path_small(sm, oracle):
     # >= 64 tokens per expert selects the prefill shape; small dims keep the oracle quick
     say("moe prefill small")
