@@ -149,7 +149,9 @@ int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
  * seedmm_moe_timed -- seedmm_moe that also records caller-created hipEvent_t handles on
  * hip_stream between its kernels, for measuring each stage in place:
  *   events[0] before the dispatch, events[1] after it, events[2] after the gate/up
- *   kernel, events[3] after the down kernel, events[4] after the combine.
+ *   kernel, events[3] after the down kernel, events[4] after the combine.  A one-token
+ *   batch (T = 1) runs no dispatch kernel (its top_k ids name the experts directly), so
+ *   events[0] and events[1] are recorded back to back.
  * `events` may be NULL and any entry may be NULL.  Same arguments, results and errors
  * as seedmm_moe; no event is recorded when the arguments are rejected.
  */

@@ -277,7 +277,14 @@ struct MfmaArgs {
     float* y;               // GEMM: fp32 [N][ldy]; DOWN: fp32 [T*top_k][ldy]
     uint16_t* h;            // GATEUP: bf16 [T*top_k][ldy]
     int ldy;
+    const int32_t* ids;     // one token (T = 1): topk_ids, workgroup y serves slot y
 };
+
+// Pair lists of the one-token path: slot y's list is the single pair index y.
+__device__ const int32_t kSlotIota[64] = {
+    0,  1,  2,  3,  4,  5,  6,  7,  8,  9,  10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21,
+    22, 23, 24, 25, 26, 27, 28, 29, 30, 31, 32, 33, 34, 35, 36, 37, 38, 39, 40, 41, 42, 43,
+    44, 45, 46, 47, 48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 58, 59, 60, 61, 62, 63};
 
 // Per-lane state of one pass over K.
 struct Lane {
@@ -418,7 +425,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2
     // ---- which expert this workgroup serves --------------------------------------
     int e = 0, n_e = a.N;
     const int32_t* list = nullptr;
-    if constexpr (MODE != MODE_GEMM) {
+    if (MODE != MODE_GEMM && a.ids) {
+        // one token: its top_k slots are top_k distinct experts, one workgroup row each
+        e = a.ids[blockIdx.y];
+        if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
+        n_e = 1;
+        list = kSlotIota + blockIdx.y;
+    } else if constexpr (MODE != MODE_GEMM) {
         const int target = blockIdx.y;
         int found = -1, cum = 0;
         for (int base = 0; base < a.E && found < 0; base += 64) {
@@ -1037,12 +1050,16 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     auto mark = [&](int i) {
         if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
     };
+    // one token: the expert kernels read its top_k ids directly (no dispatch)
+    const bool one = T == 1;
     mark(0);
-    hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T, counts, lists);
+    if (!one)
+        hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T, counts,
+                           lists);
     mark(1);
 
     const int pairs = T * top_k;
-    const int gridy = pairs < E ? pairs : E;          // at most this many active experts
+    const int gridy = one ? top_k : (pairs < E ? pairs : E);   // workgroup rows
     const bool prefill = (int64_t)pairs >= 64LL * E;  // >= 64 tokens per expert on average
     bool vec = true;
     for (const seedmm_mat* m : mats) vec = vec && use_vec(m->seeds, m->coefs, m->codes, 64);
@@ -1054,6 +1071,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     a.x = (const uint16_t*)x; a.ldx = H;
     a.counts = counts; a.lists = lists; a.E = E; a.T = T; a.top_k = top_k;
     a.h = hbuf; a.ldy = I;
+    a.ids = one ? topk_ids : nullptr;
     mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
     mark(2);
 
@@ -1063,6 +1081,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     b.x = hbuf; b.ldx = I;
     b.counts = counts; b.lists = lists; b.E = E; b.T = T; b.top_k = top_k;
     b.topk_w = topk_w; b.y = obuf; b.ldy = H;
+    b.ids = a.ids;
     mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
     mark(3);
 

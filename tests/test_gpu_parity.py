@@ -263,6 +263,10 @@ def test_moe_output_independent_of_batch(sm):
     y_big, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)        # 1032 pairs
     y_small, _ = run_moe(sm, gate, up, down, ids[:128], w[:128], x[:128], E, H, I, P)
     assert np.array_equal(y_small.view(np.uint32), y_big[:128].view(np.uint32))
+    # one token takes the dispatch-free path (its top_k slots name the experts)
+    for t in (0, 77):
+        y_one, _ = run_moe(sm, gate, up, down, ids[t:t + 1], w[t:t + 1], x[t:t + 1], E, H, I, P)
+        assert np.array_equal(y_one.view(np.uint32), y_big[t:t + 1].view(np.uint32)), t
 
 
 def test_moe_graph_replays_match_eager(sm):
