@@ -346,11 +346,11 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
 }
 
 // One pass: NTA tiles of 16 tokens starting at token slot `pass`.
-template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB>
+template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB, int RT>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, const int32_t* list,
                                           int n_e, int pass, int m0, int wave, int lane, int r,
                                           f32x4 (*red)[NT][64]) {
-    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4;   // waves sharing one matrix's K range
+    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;   // waves sharing one K range
     // B rows of this lane (token column r of every tile); slots past n_e repeat the last
     // token so every load stays in range -- their outputs are never stored.
     const uint16_t* brow[NTA];
@@ -368,19 +368,25 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
     for (int t = 0; t < NTA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     mfma_k_loop<P, VEC, NTA, KS, TAB>(L, brow, acc);
 
-    // partial sums of the four waves meet in LDS; wave t % 4 finishes tile t
+    // partial sums of the four waves meet in LDS (fixed order); wave c % 4 finishes the
+    // (row tile, token tile) pair c
 #pragma unroll
     for (int t = 0; t < NTA; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < NTA; ++t) {
-        if ((t & 3) != wave) continue;
+    for (int c = 0; c < RT * NTA; ++c) {
+        if ((c & 3) != wave) continue;
+        const int rt = c % RT, t = c / RT;
         f32x4 v, v2;
         if constexpr (MODE == MODE_GATEUP) {
             v = red[0][t][lane] + red[1][t][lane];      // gate
             v2 = red[2][t][lane] + red[3][t][lane];     // up
-        } else {
+        } else if constexpr (KS == 4) {
             v = ((red[0][t][lane] + red[1][t][lane]) + red[2][t][lane]) + red[3][t][lane];
+        } else if constexpr (KS == 2) {
+            v = red[2 * rt][t][lane] + red[2 * rt + 1][t][lane];
+        } else {
+            v = red[rt][t][lane];
         }
         const int i = pass + 16 * t + r;     // D column = token slot
         if (i >= n_e) continue;
@@ -392,7 +398,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
             dst = list[i];
             if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
         }
-        const int mq = m0 + 4 * (lane >> 4);   // D rows mq .. mq+3
+        const int mq = m0 + 16 * rt + 4 * (lane >> 4);   // D rows mq .. mq+3
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = mq + j;
@@ -412,9 +418,10 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
 
 // 4 waves on 16 weight rows.  GATEUP: waves 0-1 regenerate gate, waves 2-3 up, each
 // over half of K; otherwise the 4 waves take a quarter of K each.
-template <int P, bool VEC, int NT, int MODE, bool TAB>
+template <int P, bool VEC, int NT, int MODE, bool TAB, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2))) void k_mfma(const MfmaArgs a) {
-    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4;
+    static_assert(MODE != MODE_GATEUP || RT == 1, "gate/up pairs its waves by matrix");
+    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;
     __shared__ f32x4 red[4][NT][64];
     __shared__ uint32_t tab[TAB ? 512 : 1];
     if constexpr (TAB) fill_lfsr_tables(tab);
@@ -462,8 +469,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2
     const int64_t nblk = (int64_t)a.M * L.nbpr;
     if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true);
     else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
-    const int m0 = blockIdx.x * 16;
-    const int row = m0 + r;
+    const int m0 = blockIdx.x * 16 * RT;
+    const int row = m0 + 16 * (wave / KS % RT) + r;
     L.rv = row < a.M;
     L.rowb = (int64_t)(L.rv ? row : a.M - 1) * L.nbpr;
     L.nseg = (L.nbpr + 7) / 8;
@@ -473,10 +480,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2
         const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
         static_assert(NT == 4, "the decode kernel holds at most 4 token tiles");
         switch (ntiles) {
-            case 1: mfma_pass<P, VEC, 1, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
-            case 2: mfma_pass<P, VEC, 2, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
-            case 3: mfma_pass<P, VEC, 3, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
-            default: mfma_pass<P, VEC, 4, MODE, NT, TAB>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            case 1: mfma_pass<P, VEC, 1, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            case 2: mfma_pass<P, VEC, 2, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            case 3: mfma_pass<P, VEC, 3, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            default: mfma_pass<P, VEC, 4, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
         }
     }
 }
@@ -892,8 +899,10 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
         dim3 grid((a.M + RM - 1) / RM, gridy);
         hipLaunchKernelGGL((k_wide<P, MODE>), grid, dim3(512), 0, st, a);
     } else {
-        dim3 grid((a.M + 15) / 16, gridy);
-        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, true>), grid, dim3(256), 0, st, a);
+        // down and the plain product: two 16-row tiles per workgroup, K in halves
+        constexpr int RT = MODE == MODE_GATEUP ? 1 : 2;
+        dim3 grid((a.M + 16 * RT - 1) / (16 * RT), gridy);
+        hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, true, RT>), grid, dim3(256), 0, st, a);
     }
 }
 
