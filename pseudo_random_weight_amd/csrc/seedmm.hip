@@ -786,21 +786,17 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
 
 // ----------------------------------------------------------------------------------
 // MoE dispatch: workgroup e compacts the pairs routed to expert e, in pair order.
-// Thread t owns the contiguous run of pairs [t*R, (t+1)*R): it counts its matches, a
-// workgroup prefix sum of the counts gives its first output slot, and a second pass
-// over the run writes the pair indices.  Two round trips to memory, one barrier, no
-// atomics: the lists are deterministic.
+// The ids are staged through LDS in tiles of 8192 with coalesced loads; within a tile
+// thread t owns the contiguous run [t*R, (t+1)*R): it counts its matches, a workgroup
+// prefix sum of the counts (plus the matches of earlier tiles) gives its first output
+// slot, and a second pass over the run writes the pair indices.  No atomics: the lists
+// are deterministic.  The tile is stored with one padding word per 32 so that the 64
+// runs a wave reads at once fall in different banks.
 // ----------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_dispatch(const int32_t* __restrict__ ids, int total,
-                                                  int T, int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ lists) {
-    __shared__ int wsum[4];
-    const int e = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int R = (total + 255) / 256;
-    const int p0 = min(tid * R, total), p1 = min(p0 + R, total);
-    int c = 0;
-    for (int p = p0; p < p1; ++p) c += ids[p] == e;
+// Exclusive prefix of per-thread counts over a 256-thread workgroup (wave shuffles, then
+// the four wave totals through LDS); `total` receives the sum.  Contains a barrier.
+__device__ __forceinline__ int wg_exclusive_scan(int c, int* wsum, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = c;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -809,21 +805,58 @@ __global__ __launch_bounds__(256) void k_dispatch(const int32_t* __restrict__ id
     }
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int slot = incl - c;
-    for (int w = 0; w < wave; ++w) slot += wsum[w];
+    int excl = incl - c;
+    for (int w = 0; w < wave; ++w) excl += wsum[w];
+    total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    return excl;
+}
+
+constexpr int kDispTile = 8192;
+
+__device__ __forceinline__ int disp_slot(int i) { return i + (i >> 5); }
+
+__global__ __launch_bounds__(256) void k_dispatch(const int32_t* __restrict__ ids, int total,
+                                                  int T, int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ lists) {
+    __shared__ int32_t s_ids[kDispTile + kDispTile / 32];
+    __shared__ int wsum[4];
+    const int e = blockIdx.x, tid = threadIdx.x;
     int32_t* out = lists + (int64_t)e * T;
-    if (c > 0) {
-        for (int p = p0; p < p1; ++p) {
-            if (ids[p] == e) {
-                if (slot < T) out[slot] = p;   // ids repeated within a token: dropped
-                ++slot;
+    int done = 0;   // matches in earlier tiles
+    for (int t0 = 0; t0 < total; t0 += kDispTile) {
+        const int n = min(kDispTile, total - t0);
+        {   // all of a thread's loads in flight at once, then the LDS stores
+            int32_t v[kDispTile / 256];
+#pragma unroll
+            for (int k = 0; k < kDispTile / 256; ++k) {
+                const int i = tid + 256 * k;
+                v[k] = i < n ? ids[t0 + i] : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < kDispTile / 256; ++k) {
+                const int i = tid + 256 * k;
+                if (i < n) s_ids[disp_slot(i)] = v[k];
             }
         }
+        __syncthreads();
+        const int R = (n + 255) / 256;
+        const int p0 = min(tid * R, n), p1 = min(p0 + R, n);
+        int c = 0;
+        for (int p = p0; p < p1; ++p) c += s_ids[disp_slot(p)] == e;
+        int tile_total;
+        int slot = done + wg_exclusive_scan(c, wsum, tile_total);
+        if (c > 0) {
+            for (int p = p0; p < p1; ++p) {
+                if (s_ids[disp_slot(p)] == e) {
+                    if (slot < T) out[slot] = t0 + p;   // ids repeated within a token: dropped
+                    ++slot;
+                }
+            }
+        }
+        done += tile_total;
+        __syncthreads();   // the tile and wsum are reused
     }
-    if (tid == 0) {
-        const int n = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        counts[e] = n < T ? n : T;
-    }
+    if (tid == 0) counts[e] = done < T ? done : T;
 }
 
 // y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.

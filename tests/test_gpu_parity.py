@@ -175,7 +175,8 @@ def test_gemv_ex_bf16_shapes(sm, oracle, P, M, K):
 
 def test_dispatch_groups_pairs_in_order(sm):
     import torch
-    for (T, E, k) in [(1, 100, 8), (64, 100, 8), (37, 5, 3), (4096, 100, 8), (3, 16, 1)]:
+    for (T, E, k) in [(1, 100, 8), (64, 100, 8), (37, 5, 3), (4096, 100, 8), (3, 16, 1),
+                      (1500, 10, 7)]:
         say("dispatch", T, E, k)
         ids, _ = synth.route_topk(synth.config_seed(2), f"d{T}", T, E, k)
         counts, lists = sm.moe_dispatch(torch.from_numpy(ids).cuda(), E)
