@@ -59,6 +59,8 @@ def lib():
                                            p, f64, p, i32, i32, i32]
         L.seedref_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32] + [p] * 12
         L.seedref_search_block.argtypes = [p, i32, i32, p, p, p, p]
+        L.seedref_search_block_w.argtypes = [p, p, i32, i32, p, p, p, p]
+        L.seedref_search_matrix.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p]
         L.seedref_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,15 +187,41 @@ def moe(topk_ids: np.ndarray, topk_w: np.ndarray, x: np.ndarray, E: int, H: int,
     return y
 
 
-def search_block(w8: np.ndarray, exp_bias: int, P: int):
+def search_block(w8: np.ndarray, exp_bias: int, P: int, d8: np.ndarray = None):
+    """(seed, coefficients, code, squared error) of the exhaustive search for one block;
+    d8: importance of each of the 8 weights (None: unweighted)."""
     w = np.ascontiguousarray(w8, dtype=np.float64)
     seed = np.zeros(1, dtype=np.uint16)
     c = np.zeros(4, dtype=np.int32)
     cd = np.zeros(1, dtype=np.int32)
     err = np.zeros(1, dtype=np.float64)
-    _check(lib().seedref_search_block(_ptr(w), exp_bias, P, _ptr(seed), _ptr(c), _ptr(cd),
-                                      _ptr(err)), "search_block")
+    if d8 is None:
+        rc = lib().seedref_search_block(_ptr(w), exp_bias, P, _ptr(seed), _ptr(c), _ptr(cd),
+                                        _ptr(err))
+    else:
+        d = np.ascontiguousarray(d8, dtype=np.float64)
+        rc = lib().seedref_search_block_w(_ptr(w), _ptr(d), exp_bias, P, _ptr(seed), _ptr(c),
+                                          _ptr(cd), _ptr(err))
+    _check(rc, "search_block")
     return int(seed[0]), [int(v) for v in c[:P]], int(cd[0]), float(err[0])
+
+
+def search_matrix(W: np.ndarray, P: int, exp_bias: int, colw: np.ndarray = None):
+    """Encode fp32 W [M][K] block by block: a seed-coded matrix dict (seeds, coefs,
+    codes, exp_bias) plus the squared error of every block ('err', float64 [M*K/8])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    M, K = W.shape
+    nblk = M * (K // 8)
+    seeds = np.zeros(nblk, dtype=np.uint16)
+    coefs = np.zeros((nblk * P + 3) // 4, dtype=np.uint16)
+    codes = np.zeros((nblk + 1) // 2, dtype=np.uint8)
+    err = np.zeros(nblk, dtype=np.float64)
+    cw = None if colw is None else np.ascontiguousarray(colw, dtype=np.float32)
+    _check(lib().seedref_search_matrix(_ptr(W), None if cw is None else _ptr(cw), M, K, P,
+                                       exp_bias, _ptr(seeds), _ptr(coefs), _ptr(codes),
+                                       _ptr(err)), "search_matrix")
+    return {"seeds": seeds, "coefs": coefs, "codes": codes,
+            "exp_bias": np.array([exp_bias], dtype=np.int32), "err": err}
 
 
 def num_threads() -> int:

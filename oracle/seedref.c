@@ -311,10 +311,12 @@ static int solve_small(double a[4][4], double r[4], int P, double x[4])
 
 /* [P4CARD "How it works"], [K2CARD "This upload"]: the search tries all 65,535 seeds per
  * block and keeps the one whose basis comes nearest to the original weights; [BLOG
- * "GPU search == CPU search"]: no contraction.  Unweighted here (the activation weighting
- * of the real encoder needs calibration data). */
-int seedref_search_block(const double *w8, int exp_bias, int P, uint16_t *seed_out,
-                         int *c_out, int *code_out, double *err_out)
+ * "GPU search == CPU search"]: no contraction.  d8 (may be NULL: all ones) weights the
+ * squared error of each of the 8 weights, as an activation-importance weighting does:
+ *   A_jk = sum_i (d_i U_ij) U_ik,  r_j = sum_i (d_i U_ij) w_i,  err = sum_i d_i (w_i - sc v_i)^2
+ * with every sum taken in increasing i. */
+int seedref_search_block_w(const double *w8, const double *d8, int exp_bias, int P,
+                           uint16_t *seed_out, int *c_out, int *code_out, double *err_out)
 {
     if (P != 3 && P != 4)
         return -1;
@@ -331,11 +333,11 @@ int seedref_search_block(const double *w8, int exp_bias, int P, uint16_t *seed_o
         for (int j = 0; j < P; ++j) {
             r[j] = 0.0;
             for (int i = 0; i < 8; ++i)
-                r[j] += U[i][j] * w8[i];
+                r[j] += (d8 ? d8[i] * U[i][j] : U[i][j]) * w8[i];
             for (int k = 0; k < P; ++k) {
                 a[j][k] = 0.0;
                 for (int i = 0; i < 8; ++i)
-                    a[j][k] += U[i][j] * U[i][k];
+                    a[j][k] += (d8 ? d8[i] * U[i][j] : U[i][j]) * U[i][k];
             }
         }
         if (solve_small(a, r, P, alpha) != 0)
@@ -355,7 +357,7 @@ int seedref_search_block(const double *w8, int exp_bias, int P, uint16_t *seed_o
                 for (int j = 0; j < P; ++j)
                     v += U[i][j] * (double)c[j];
                 double d = w8[i] - sc * v;
-                err += d * d;
+                err += d8 ? d8[i] * (d * d) : d * d;
             }
             if (err < best_err) {      /* strict: ties keep the lower (seed, code) */
                 best_err = err;
@@ -374,6 +376,65 @@ int seedref_search_block(const double *w8, int exp_bias, int P, uint16_t *seed_o
         c_out[j] = best_c[j];
     *err_out = best_err;
     return 0;
+}
+
+int seedref_search_block(const double *w8, int exp_bias, int P, uint16_t *seed_out,
+                         int *c_out, int *code_out, double *err_out)
+{
+    return seedref_search_block_w(w8, NULL, exp_bias, P, seed_out, c_out, code_out, err_out);
+}
+
+/* The search over every block of an [M][K] matrix (K % 8 == 0): seeds, the coefficient
+ * nibble stream and the code stream in the layout seedref_reconstruct_f32 reads, and the
+ * squared error of every block.  colw: per-column importance (length K) or NULL.
+ * Blocks are independent; OpenMP spreads them over threads. */
+int seedref_search_matrix(const float *W, const float *colw, int M, int K, int P,
+                          int exp_bias, uint16_t *seeds, uint16_t *coefs, uint8_t *codes,
+                          double *err)
+{
+    if (M < 0 || K < 0 || K % 8 != 0 || (P != 3 && P != 4))
+        return -1;
+    const long nblk = (long)M * (K / 8);
+    memset(coefs, 0, sizeof(uint16_t) * (size_t)((nblk * P + 3) / 4));
+    memset(codes, 0, (size_t)((nblk + 1) / 2));
+    int bad = 0;
+    int *cs = (int *)malloc(sizeof(int) * (size_t)(nblk > 0 ? nblk : 1) * 5);
+    if (!cs)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long b = 0; b < nblk; ++b) {
+        const long m = b / (K / 8), kb = b % (K / 8);
+        double w8[8], d8[8];
+        for (int i = 0; i < 8; ++i) {
+            w8[i] = (double)W[m * K + 8 * kb + i];
+            if (colw)
+                d8[i] = (double)colw[8 * kb + i];
+        }
+        uint16_t sd;
+        int c[4], code;
+        double e;
+        if (seedref_search_block_w(w8, colw ? d8 : NULL, exp_bias, P, &sd, c, &code, &e) != 0) {
+            bad = 1;
+            continue;
+        }
+        seeds[b] = sd;
+        for (int j = 0; j < P; ++j)
+            cs[b * 5 + j] = c[j];
+        cs[b * 5 + 4] = code;
+        if (err)
+            err[b] = e;
+    }
+    if (!bad) {   /* packing is sequential: neighbouring blocks share words and bytes */
+        for (long b = 0; b < nblk; ++b) {
+            for (int j = 0; j < P; ++j) {
+                const long n = b * P + j;
+                coefs[n >> 2] |= (uint16_t)(((unsigned)cs[b * 5 + j] & 0xFu) << (4 * (n & 3)));
+            }
+            codes[b >> 1] |= (uint8_t)(((unsigned)cs[b * 5 + 4] & 0xFu) << (4 * (b & 1)));
+        }
+    }
+    free(cs);
+    return bad ? -1 : 0;
 }
 
 int seedref_num_threads(void)

@@ -93,6 +93,19 @@ int seedref_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
 int seedref_search_block(const double *w8, int exp_bias, int P, uint16_t *seed_out,
                          int *c_out, int *code_out, double *err_out);
 
+/* The same search with a per-weight importance d8 (NULL = all ones): the normal
+ * equations and the error are weighted, A_jk = sum_i (d_i U_ij) U_ik,
+ * r_j = sum_i (d_i U_ij) w_i, err = sum_i d_i (w_i - sc v_i)^2, sums in increasing i. */
+int seedref_search_block_w(const double *w8, const double *d8, int exp_bias, int P,
+                           uint16_t *seed_out, int *c_out, int *code_out, double *err_out);
+
+/* Search every block of W [M][K] (fp32, K % 8 == 0; colw: importance per column, length
+ * K, or NULL) and write the seeds, coefficient and code streams, and each block's
+ * squared error (err may be NULL).  Returns 0, or -1 on bad arguments. */
+int seedref_search_matrix(const float *W, const float *colw, int M, int K, int P,
+                          int exp_bias, uint16_t *seeds, uint16_t *coefs, uint8_t *codes,
+                          double *err);
+
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int seedref_num_threads(void);
 

@@ -370,3 +370,88 @@ def test_search_finds_nearest_for_a_perturbed_block(oracle):
     s2, c2, code2, err = oracle.search_block(w, -4, 4)
     assert (s2, c2, code2) == (seed, c, code_)
     assert err > 0
+
+
+def _all_states(P):
+    """States s_1..s_8P of every seed 1..65535, by a vectorised register written here
+    from the polynomial x^16 + x^14 + x^13 + x^11 + 1 (shift left, feedback into bit 0)."""
+    s = np.arange(1, 65536, dtype=np.uint32)
+    out = np.empty((65535, 8 * P), dtype=np.int64)
+    for t in range(8 * P):
+        fb = ((s >> 15) ^ (s >> 13) ^ (s >> 12) ^ (s >> 10)) & 1
+        s = ((s << 1) | fb) & 0xFFFF
+        out[:, t] = s
+    return out
+
+
+def _brute_force_search(w8, P, exp_bias, d8):
+    """Every seed's least-squares coefficients (numpy solve), every code's rounded and
+    clamped coefficients, and the weighted squared error of each candidate."""
+    U = (_all_states(P) - 32768).astype(np.float64).reshape(65535, 8, P)
+    d = np.ones(8) if d8 is None else np.asarray(d8, dtype=np.float64)
+    A = np.einsum("sij,i,sik->sjk", U, d, U)
+    r = np.einsum("sij,i,i->sj", U, d, w8)
+    full = np.linalg.matrix_rank(A) == P       # singular systems have no LS solution
+    alpha = np.zeros((65535, P))
+    alpha[full] = np.linalg.solve(A[full], r[full][..., None])[..., 0]
+    best = (np.inf, None, None)
+    for code in range(16):
+        sc = 2.0 ** (code + exp_bias - 15)
+        c = np.clip(np.rint(alpha / sc), -8, 7)
+        v = np.einsum("sij,sj->si", U, c)
+        err = ((w8[None, :] - sc * v) ** 2 * d[None, :]).sum(axis=1)
+        err[~full] = np.inf
+        i = int(np.argmin(err))
+        if err[i] < best[0]:
+            best = (float(err[i]), i + 1, code)
+    return best
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_search_picks_the_brute_force_minimum(oracle, weighted):
+    # an independent re-derivation of the search (numpy LFSR, batched solve): the oracle's
+    # choice reaches the smallest squared error over all 65,535 x 16 candidates
+    rng = np.random.default_rng(77 + weighted)
+    for P in (4, 3):
+        w8 = rng.standard_normal(8) * 0.05
+        d8 = rng.uniform(0.1, 3.0, 8) if weighted else None
+        s2, c2, code2, err = oracle.search_block(w8, -4, P, d8)
+        ref_err, ref_seed, ref_code = _brute_force_search(w8, P, -4, d8)
+        assert err == pytest.approx(ref_err, rel=1e-9, abs=1e-300)
+        assert (s2, code2) == (ref_seed, ref_code)
+        # the reported error is the error of the returned encoding
+        blk = oracle.block(s2, c2, P, code2, -4).astype(np.float64)
+        d = np.ones(8) if d8 is None else d8
+        assert err == pytest.approx(float((d * (w8 - blk) ** 2).sum()), rel=1e-12)
+
+
+def test_weighted_search_with_unit_weights_is_the_unweighted_search(oracle):
+    rng = np.random.default_rng(5)
+    for P in (4, 3):
+        w8 = rng.standard_normal(8) * 0.02
+        assert oracle.search_block(w8, -4, P, np.ones(8)) == oracle.search_block(w8, -4, P)
+
+
+@pytest.mark.parametrize("P", [4, 3])
+def test_weighted_search_recovers_a_planted_block(oracle, P):
+    # an exact encoding has zero error under any positive weighting
+    rng = np.random.default_rng(300 + P)
+    c = [7, -8, 3, -5][:P]
+    seed, code_ = int(rng.integers(1, 65536)), 6
+    w = oracle.block(seed, c, P, code_, -4).astype(np.float64)
+    s2, c2, code2, err = oracle.search_block(w, -4, P, rng.uniform(0.2, 5.0, 8))
+    assert err == 0.0 and (s2, c2, code2) == (seed, c, code_)
+
+
+@pytest.mark.parametrize("P", [4, 3])
+def test_search_matrix_round_trips_a_seed_coded_matrix(oracle, P):
+    # W decoded from random streams is an exact fit block by block: encoding it again
+    # gives streams that decode to W bit for bit, with zero error everywhere; the P = 3
+    # nibble stream (4 blocks per 3 words) and the 2-codes-per-byte stream are packed
+    # across block boundaries here
+    M, K = 3, 24
+    mat = synth.seed_matrix(synth.config_seed(9), f"rt{P}", M, K, P)
+    W = oracle.reconstruct_f32(mat, M, K, P)
+    enc = oracle.search_matrix(W, P, -4)
+    np.testing.assert_array_equal(enc["err"], 0.0)
+    np.testing.assert_array_equal(oracle.reconstruct_f32(enc, M, K, P), W)
