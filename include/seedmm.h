@@ -161,6 +161,32 @@ int seedmm_moe_timed(const int32_t *topk_ids, const float *topk_w, int T, int to
                      void *workspace, size_t workspace_bytes, void *hip_stream,
                      void *const *events);
 
+/*
+ * seedmm_search -- encode W [M][K] into a seed-coded matrix by the exhaustive seed search
+ * (Qwen3.8-Flash-Next-NanoSeedLM-P4 card, "How it works": every one of the 65,535 seeds
+ * is tried for every block; barnson.org post, "GPU search == CPU search").  For each
+ * block of 8 weights w (with importances d, all ones when colw is NULL) and every seed:
+ *   U_ij = s_{iP+j+1} - 32768 (the states the products regenerate);
+ *   alpha solves A alpha = r, A_jk = sum_i (d_i U_ij) U_ik, r_j = sum_i (d_i U_ij) w_i, by
+ *   Gaussian elimination with partial pivoting (a pivot below 1e-300 skips the seed);
+ *   for every code 0..15: c_j = clamp(round_half_even(alpha_j / 2^(code+exp_bias-15)),
+ *   -8, 7), err = sum_i d_i (w_i - 2^(code+exp_bias-15) sum_j U_ij c_j)^2;
+ * and keeps the smallest (err, seed, code).  Every step is an IEEE double operation in
+ * that order (sums in increasing i, no contraction), so the result equals a CPU
+ * evaluation of the same definition bit for bit.
+ *   W: fp32 row-major [M][ldw] (ldw >= K), K % 8 == 0;  colw: fp32 [K] importances of
+ *   the columns (activation weighting) or NULL;  outputs in the layout the products
+ *   read: seeds uint16[M*K/8], coefs uint16[ceil(M*K/8*P/4)], codes uint8[ceil(M*K/16)],
+ *   err: float64[M*K/8] squared error of each block (may be NULL).  A block for which
+ *   no seed gives a solvable system gets seed 0, zero coefficients and err = +inf.
+ *   Compute: about 1.1e8 double operations per block.
+ * Errors: SEEDMM_EINVAL (null pointer, bad size, P not 3/4, exp_bias outside [-100, 100],
+ * ldw < K), SEEDMM_EHIP.
+ */
+int seedmm_search(const float *W, int ldw, const float *colw, int M, int K, int P,
+                  int32_t exp_bias, uint16_t *seeds, uint16_t *coefs, uint8_t *codes,
+                  double *err, void *hip_stream);
+
 /* Static description of a status code. */
 const char *seedmm_strerror(int status);
 

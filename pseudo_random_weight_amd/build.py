@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libseedmm.so")
-SOURCES = [os.path.join(CSRC, "seedmm.hip")]
+SOURCES = [os.path.join(CSRC, "seedmm.hip"), os.path.join(CSRC, "search.hip")]
 HEADERS = [os.path.join(CSRC, "seed_decode.hpp"), os.path.join(ROOT, "include", "seedmm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,12 +41,12 @@ def build(verbose: bool = False) -> str:
     return SO
 
 
-def asm(out: str = None) -> str:
-    """Device assembly of the library (for inspecting the generated gfx950 code)."""
-    out = out or os.path.join(ROOT, "_work", "seedmm.s")
+def asm(source: str = "seedmm.hip", out: str = None) -> str:
+    """Device assembly of one source file (for inspecting the generated gfx950 code)."""
+    out = out or os.path.join(ROOT, "_work", os.path.splitext(source)[0] + ".s")
     os.makedirs(os.path.dirname(out), exist_ok=True)
     cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-S",
-           "--cuda-device-only", *SOURCES, "-o", out]
+           "--cuda-device-only", os.path.join(CSRC, source), "-o", out]
     subprocess.check_call(cmd)
     return out
 

@@ -1,0 +1,245 @@
+// search.hip -- gfx950 encoder: the exhaustive seed search of SeedLM over a whole matrix.
+//
+// For one block of 8 weights w (and optional importances d), every seed 1..65535 gives
+// a basis U (8 x P, U_ij = s_{iP+j+1} - 32768, the same states the decode kernels
+// regenerate).  The weighted least-squares coefficients alpha solve
+//     A alpha = r,   A_jk = sum_i (d_i U_ij) U_ik,   r_j = sum_i (d_i U_ij) w_i,
+// by Gaussian elimination with partial pivoting (a pivot below 1e-300 in magnitude
+// skips the seed).  Every code 0..15 then rounds alpha / 2^(code + exp_bias - 15) half
+// to even, clamps it to [-8, 7] and measures err = sum_i d_i (w_i - 2^(...) v_i)^2 with
+// v_i = sum_j U_ij c_j.  The block keeps the smallest (err, seed, code) in that order.
+// (Qwen3.8-Flash-Next-NanoSeedLM-P4 card, "How it works": the search tries all 65,535
+// seeds per block; barnson.org post, "GPU search == CPU search": no contracted
+// multiply-adds, so the GPU search returns exactly what a CPU search returns.)
+//
+// Every floating-point step is a separately rounded IEEE double operation in the order
+// written above (sums in increasing i, contraction off), so the result is the same, bit
+// for bit, as any CPU evaluation of that definition.  Two exact shortcuts:
+//   - alpha / 2^e is computed as alpha * 2^-e (exact for the normal values involved);
+//   - v_i is an integer below 2^21 in magnitude, summed in int32 and converted exactly
+//     (a NaN coefficient, which only a degenerate system could produce, takes the
+//     integer -2^31 and the sum is formed in double instead).
+//
+// Mapping: one wave per block; lane l tries seeds 1 + l + 64 k in increasing order and
+// keeps its best candidate with a strict comparison (so ties keep its lower seed, then
+// its lower code); a wave reduction takes the lexicographic minimum.  A 256-thread
+// workgroup owns 4 consecutive blocks, whose coefficient nibbles fill whole words for
+// P = 3 and 4 and whose codes fill whole bytes, so it writes its streams without races.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/seedmm.h"
+#include "seed_decode.hpp"
+
+namespace seedmm {
+
+// Gaussian elimination with partial pivoting on a P x P system (first row with the
+// largest magnitude, strictly), rows exchanged with selects so no array is indexed at
+// run time.  Returns false for a pivot below 1e-300 in magnitude.
+template <int P>
+__device__ __forceinline__ bool solve_small(double (&a)[4][4], double (&r)[4], double (&x)[4]) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int col = 0; col < P; ++col) {
+        int piv = col;
+        double pv = fabs(a[col][col]);
+#pragma unroll
+        for (int row = col + 1; row < P; ++row) {
+            const double v = fabs(a[row][col]);
+            if (v > pv) { pv = v; piv = row; }
+        }
+        if (pv < 1e-300) return false;
+#pragma unroll
+        for (int row = col + 1; row < P; ++row) {
+            const bool sw = piv == row;
+#pragma unroll
+            for (int k = 0; k < P; ++k) {
+                const double t = a[col][k];
+                a[col][k] = sw ? a[row][k] : a[col][k];
+                a[row][k] = sw ? t : a[row][k];
+            }
+            const double t = r[col];
+            r[col] = sw ? r[row] : r[col];
+            r[row] = sw ? t : r[row];
+        }
+#pragma unroll
+        for (int row = col + 1; row < P; ++row) {
+            const double f = a[row][col] / a[col][col];
+#pragma unroll
+            for (int k = col; k < P; ++k) a[row][k] -= f * a[col][k];
+            r[row] -= f * r[col];
+        }
+    }
+#pragma unroll
+    for (int row = P - 1; row >= 0; --row) {
+        double s = r[row];
+#pragma unroll
+        for (int k = row + 1; k < P; ++k) s -= a[row][k] * x[k];
+        x[row] = s / a[row][row];
+    }
+    return true;
+}
+
+template <int P, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int64_t ldw,
+                                                const float* __restrict__ colw, int K,
+                                                int exp_bias, int64_t nblk,
+                                                uint16_t* __restrict__ seeds,
+                                                uint16_t* __restrict__ coefs,
+                                                uint8_t* __restrict__ codes,
+                                                double* __restrict__ errs) {
+#pragma clang fp contract(off)
+    __shared__ uint32_t res[4][2];   // per block: seed | code << 16, coefficient nibbles
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+    if (b < nblk) {
+        const int nbpr = K / 8;
+        const int64_t m = b / nbpr;
+        const int kb = (int)(b % nbpr);
+        double w[8], d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = (double)W[m * ldw + 8 * kb + i];
+            d[i] = WEIGHTED ? (double)colw[8 * kb + i] : 1.0;
+        }
+        double best = __builtin_inf();
+        int bkey = 0x7FFFFFFF;            // seed * 16 + code
+        uint32_t bnib = 0;
+        for (int k = 0; k < 1024; ++k) {
+            const int seed = 1 + lane + 64 * k;
+            if (seed > 65535) break;
+            const Window win = lfsr_window((uint32_t)seed);
+            int Ui[8][P];
+            double U[8][P];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    Ui[i][j] = (int)state(win, i * P + j + 1) - 32768;
+                    U[i][j] = (double)Ui[i][j];
+                }
+            double a[4][4], r[4], alpha[4];
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                r[j] = 0.0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) r[j] += (WEIGHTED ? d[i] * U[i][j] : U[i][j]) * w[i];
+#pragma unroll
+                for (int kk = 0; kk < P; ++kk) {
+                    a[j][kk] = 0.0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        a[j][kk] += (WEIGHTED ? d[i] * U[i][j] : U[i][j]) * U[i][kk];
+                }
+            }
+            if (!solve_small<P>(a, r, alpha)) continue;
+#pragma unroll 1
+            for (int code = 0; code < 16; ++code) {
+                const int e = code + exp_bias - 15;
+                const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
+                int c[P];
+                bool nan = false;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    double q = __builtin_rint(alpha[j] * inv);   // half to even
+                    if (q < -8.0) q = -8.0;
+                    if (q > 7.0) q = 7.0;
+                    nan |= q != q;
+                    c[j] = q != q ? (int)0x80000000 : (int)q;
+                }
+                double err = 0.0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    double v;
+                    if (!nan) {
+                        int vi = 0;
+#pragma unroll
+                        for (int j = 0; j < P; ++j) vi += Ui[i][j] * c[j];
+                        v = (double)vi;
+                    } else {
+                        v = 0.0;
+#pragma unroll
+                        for (int j = 0; j < P; ++j) v += U[i][j] * (double)c[j];
+                    }
+                    const double dd = w[i] - sc * v;
+                    err += WEIGHTED ? d[i] * (dd * dd) : dd * dd;
+                }
+                if (err < best) {
+                    best = err;
+                    bkey = seed * 16 + code;
+                    uint32_t nib = 0;
+#pragma unroll
+                    for (int j = 0; j < P; ++j) nib |= ((uint32_t)c[j] & 0xFu) << (4 * j);
+                    bnib = nib;
+                }
+            }
+        }
+        // lexicographic minimum of (err, seed, code) over the wave
+        const int own = bkey;
+        double gb = best;
+        int gk = bkey;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double ob = __shfl_xor(gb, off);
+            const int ok = __shfl_xor(gk, off);
+            if (ob < gb || (ob == gb && ok < gk)) { gb = ob; gk = ok; }
+        }
+        if (own == gk && gk != 0x7FFFFFFF) {
+            res[wave][0] = (uint32_t)(gk >> 4) | ((uint32_t)(gk & 15) << 16);
+            res[wave][1] = bnib;
+            if (errs) errs[b] = gb;
+        }
+        if (lane == 0 && gk == 0x7FFFFFFF) {   // no seed had a solvable system
+            res[wave][0] = 0u;
+            res[wave][1] = 0u;
+            if (errs) errs[b] = __builtin_inf();
+        }
+    }
+    __syncthreads();
+    // the group's streams: 4 seeds, 4*P nibbles (P whole words), 4 codes (2 whole bytes)
+    const int64_t b0 = (int64_t)blockIdx.x * 4;
+    const int nb = (int)(nblk - b0 < 4 ? nblk - b0 : 4);
+    const int tid = threadIdx.x;
+    if (tid < nb) seeds[b0 + tid] = (uint16_t)(res[tid][0] & 0xFFFFu);
+    if (tid < (nb * P + 3) / 4) {           // coefficient word tid of the group
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 4 * tid + q;          // nibble within the group
+            const int blk = n / P, j = n % P;
+            if (blk < nb) word |= ((res[blk][1] >> (4 * j)) & 0xFu) << (4 * q);
+        }
+        coefs[b0 * P / 4 + tid] = (uint16_t)word;
+    }
+    if (tid >= 64 && tid < 64 + (nb + 1) / 2) {   // code byte of blocks 2t, 2t+1
+        const int t = tid - 64;
+        uint32_t byte = (res[2 * t][0] >> 16) & 0xFu;
+        if (2 * t + 1 < nb) byte |= ((res[2 * t + 1][0] >> 16) & 0xFu) << 4;
+        codes[b0 / 2 + t] = (uint8_t)byte;
+    }
+}
+
+}  // namespace seedmm
+
+using namespace seedmm;
+
+extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, int K, int P,
+                             int32_t exp_bias, uint16_t* seeds, uint16_t* coefs,
+                             uint8_t* codes, double* err, void* hip_stream) {
+    if (M < 0 || K < 0 || K % 8 != 0 || (P != 3 && P != 4)) return SEEDMM_EINVAL;
+    if (exp_bias < -100 || exp_bias > 100) return SEEDMM_EINVAL;
+    if (ldw < K) return SEEDMM_EINVAL;
+    const int64_t nblk = (int64_t)M * (K / 8);
+    if (nblk == 0) return SEEDMM_OK;
+    if (!W || !seeds || !coefs || !codes) return SEEDMM_EINVAL;
+    hipStream_t st = (hipStream_t)hip_stream;
+    const dim3 grid((unsigned)((nblk + 3) / 4));
+    if (P == 4) {
+        if (colw) hipLaunchKernelGGL((k_search<4, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search<4, false>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+    } else {
+        if (colw) hipLaunchKernelGGL((k_search<3, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search<3, false>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+    }
+    return hipGetLastError() == hipSuccess ? SEEDMM_OK : SEEDMM_EHIP;
+}

@@ -46,11 +46,12 @@ def _load():
     L.seedmm_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, SeedMat, SeedMat, SeedMat,
                              p, ctypes.c_size_t, p]
     L.seedmm_moe_timed.argtypes = L.seedmm_moe.argtypes + [p]
+    L.seedmm_search.argtypes = [p, i32, p, i32, i32, i32, ctypes.c_int32, p, p, p, p, p]
     L.seedmm_strerror.restype = ctypes.c_char_p
     L.seedmm_strerror.argtypes = [i32]
     L.seedmm_version.restype = i32
     for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-                 "seedmm_moe", "seedmm_moe_timed"):
+                 "seedmm_moe", "seedmm_moe_timed", "seedmm_search"):
         getattr(L, name).restype = i32
     return L
 
@@ -58,8 +59,8 @@ def _load():
 _lib = _load()
 
 EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_strerror",
-           "seedmm_version")
+           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_search",
+           "seedmm_strerror", "seedmm_version")
 
 
 def lib():
@@ -194,3 +195,28 @@ def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None,
         arr = (ctypes.c_void_p * 5)(*[getattr(ev, "cuda_event", ev) for ev in events])
         _check(_lib.seedmm_moe_timed(*args, arr), "seedmm_moe_timed")
     return y
+
+
+def search(W: torch.Tensor, P: int, exp_bias: int, colw: torch.Tensor = None, err=True,
+           stream=None):
+    """Encode fp32 W [M][K] by the exhaustive seed search (seedmm_search): a dict with
+    seeds, coefs, codes (device tensors, the products' layout), exp_bias and, if asked,
+    err (float64 [M*K/8], squared error of every block)."""
+    _dev(W, torch.float32, "W")
+    M, K = W.shape
+    nblk = M * (K // 8)
+    dev = W.device
+    out = {"seeds": torch.empty(nblk, dtype=torch.uint16, device=dev),
+           "coefs": torch.empty((nblk * P + 3) // 4, dtype=torch.uint16, device=dev),
+           "codes": torch.empty((nblk + 1) // 2, dtype=torch.uint8, device=dev),
+           "exp_bias": torch.full((1,), exp_bias, dtype=torch.int32, device=dev),
+           "exp_bias_host": [exp_bias]}
+    e = torch.empty(nblk, dtype=torch.float64, device=dev) if err else None
+    if colw is not None:
+        _dev(colw, torch.float32, "colw")
+    _check(_lib.seedmm_search(_ptr(W), K, _ptr(colw), M, K, P, exp_bias, _ptr(out["seeds"]),
+                              _ptr(out["coefs"]), _ptr(out["codes"]), _ptr(e),
+                              _stream(stream)), "seedmm_search")
+    if err:
+        out["err"] = e
+    return out

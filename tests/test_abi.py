@@ -116,3 +116,15 @@ def test_binding_has_no_fallback():
     src = open(os.path.join(ROOT, "pseudo_random_weight_amd", "seedmm.py")).read()
     assert "import oracle" not in src and "from oracle" not in src
     assert "raise ImportError" in src
+
+
+def test_search_rejects(lib):
+    f = lib.seedmm_search
+    # (W, ldw, colw, M, K, P, exp_bias, seeds, coefs, codes, err, stream)
+    assert f(FAKE, 12, None, 4, 12, 4, -4, FAKE, FAKE, FAKE, None, None) == -1    # K % 8
+    assert f(FAKE, 16, None, 4, 16, 5, -4, FAKE, FAKE, FAKE, None, None) == -1    # P
+    assert f(FAKE, 16, None, 4, 16, 4, 101, FAKE, FAKE, FAKE, None, None) == -1   # exp_bias
+    assert f(FAKE, 8, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, None) == -1     # ldw < K
+    assert f(None, 16, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, None) == -1    # null W
+    assert f(FAKE, 16, None, 4, 16, 4, -4, FAKE, None, FAKE, None, None) == -1    # null coefs
+    assert f(None, 16, None, 0, 16, 4, -4, None, None, None, None, None) == 0     # empty

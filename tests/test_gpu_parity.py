@@ -370,3 +370,51 @@ def test_moe_is_deterministic_and_permutation_equivariant(sm):
     perm = np.random.default_rng(0).permutation(T)
     y3, _ = run_moe(sm, gate, up, down, ids[perm], w[perm], x[perm], E, H, I, P)
     np.testing.assert_array_equal(y3, y1[perm])
+
+
+# ---------------------------------------------------------------------------------
+# Encoder: the exhaustive seed search on the GPU against the oracle's search
+# ---------------------------------------------------------------------------------
+def _search_case(M, K, tag, scale=0.02):
+    base = synth.config_seed(7)
+    return (synth.normal_f32(base, tag + ".W", (M, K)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("P", [4, 3])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_search_matches_oracle_bit_for_bit(sm, oracle, P, weighted):
+    """Seeds, coefficient and code streams and every block's squared error equal the
+    oracle's search exactly (11 blocks: a ragged group of four, P = 3 words shared
+    across blocks)."""
+    import torch
+    M, K = 1, 88
+    say("search vs oracle", P, weighted)
+    W = _search_case(M, K, f"s{P}{weighted}")
+    colw = None
+    if weighted:
+        colw = np.abs(synth.normal_f32(synth.config_seed(7), f"cw{P}", (K,))).astype(np.float32) + 0.1
+    ref = oracle.search_matrix(W, P, -4, colw)
+    got = sm.search(torch.from_numpy(W).cuda(), P, -4,
+                    None if colw is None else torch.from_numpy(colw).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got["seeds"].cpu().view(torch.int16).numpy().view(np.uint16), ref["seeds"])
+    np.testing.assert_array_equal(got["coefs"].cpu().view(torch.int16).numpy().view(np.uint16), ref["coefs"])
+    np.testing.assert_array_equal(got["codes"].cpu().numpy(), ref["codes"])
+    np.testing.assert_array_equal(got["err"].cpu().numpy().view(np.uint64), ref["err"].view(np.uint64))
+
+
+@pytest.mark.parametrize("P", [4, 3])
+def test_search_recovers_a_seed_coded_matrix(sm, oracle, P):
+    """A matrix decoded from random streams is an exact fit: the GPU encoding decodes back
+    to it bit for bit (GPU reconstruct) with zero error in every block."""
+    import torch
+    M, K = 5, 64
+    say("search planted matrix", P)
+    mat = synth.seed_matrix(synth.config_seed(8), f"pl{P}", M, K, P)
+    W = oracle.reconstruct_f32(mat, M, K, P)
+    got = sm.search(torch.from_numpy(W).cuda(), P, -4)
+    torch.cuda.synchronize()
+    assert float(got["err"].abs().max()) == 0.0
+    Wg = sm.reconstruct(got, M, K, P)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wg.cpu().numpy(), W)
