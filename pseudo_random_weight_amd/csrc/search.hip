@@ -14,11 +14,13 @@
 //
 // Every floating-point step is a separately rounded IEEE double operation in the order
 // written above (sums in increasing i, contraction off), so the result is the same, bit
-// for bit, as any CPU evaluation of that definition.  Two exact shortcuts:
+// for bit, as any CPU evaluation of that definition.  Three exact shortcuts:
 //   - alpha / 2^e is computed as alpha * 2^-e (exact for the normal values involved);
 //   - v_i is an integer below 2^21 in magnitude, summed in int32 and converted exactly
 //     (a NaN coefficient, which only a degenerate system could produce, takes the
-//     integer -2^31 and the sum is formed in double instead).
+//     integer -2^31 and the sum is formed in double instead);
+//   - once every coefficient of a seed rounds to zero, all larger codes do too and all
+//     have the same error (that of zero coefficients), so only the first is compared.
 //
 // Mapping: one wave per block; lane l tries seeds 1 + l + 64 k in increasing order and
 // keeps its best candidate with a strict comparison (so ties keep its lower seed, then
@@ -102,6 +104,13 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
             w[i] = (double)W[m * ldw + 8 * kb + i];
             d[i] = WEIGHTED ? (double)colw[8 * kb + i] : 1.0;
         }
+        // error of the all-zero coefficients, summed exactly as the code loop sums it
+        double e0 = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double dd = w[i] - 0.0;
+            e0 += WEIGHTED ? d[i] * (dd * dd) : dd * dd;
+        }
         double best = __builtin_inf();
         int bkey = 0x7FFFFFFF;            // seed * 16 + code
         uint32_t bnib = 0;
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
                 const int e = code + exp_bias - 15;
                 const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
                 int c[P];
-                bool nan = false;
+                bool nan = false, zero = true;
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
                     double q = __builtin_rint(alpha[j] * inv);   // half to even
@@ -146,6 +155,18 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
                     if (q > 7.0) q = 7.0;
                     nan |= q != q;
                     c[j] = q != q ? (int)0x80000000 : (int)q;
+                    zero &= c[j] == 0;
+                }
+                if (zero) {
+                    // |alpha_j| / 2^e only shrinks as the code grows, so every larger code
+                    // rounds to zero as well; they all have error e0 and, compared
+                    // strictly, none of them can replace this one
+                    if (e0 < best) {
+                        best = e0;
+                        bkey = seed * 16 + code;
+                        bnib = 0;
+                    }
+                    break;
                 }
                 double err = 0.0;
 #pragma unroll
