@@ -16,7 +16,8 @@ that captures its decode step would run it (--eager times the eager launches ins
 
 Prints one JSON line: effective weights/s (distinct expert weights applied per second),
 compressed HBM GB/s and its fraction of 8 TB/s, decode tokens/s, the roofline, and the
-CPU oracle timed on a bounded sample of the same step.
+CPU oracle timed on a bounded sample of the same step; "encoder" adds the exhaustive
+seed search's blocks/s on a 512 x 2048 matrix beside the oracle's search.
 """
 from __future__ import annotations
 
@@ -52,6 +53,8 @@ def parse():
                     help="run one plain device copy of this size (counter calibration)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
+    ap.add_argument("--no-encoder", action="store_true",
+                    help="skip the seed-search (encoder) measurement")
     return ap.parse_args()
 
 
@@ -115,6 +118,38 @@ class HipEvents:
         for h in self.live:
             self.hip.hipEventDestroy(self.ct.c_void_p(h))
         self.live = []
+
+
+def encoder_bench(torch, seedmm, synth, P, no_cpu):
+    """The exhaustive seed search (seedmm_search) on a synthetic fp32 matrix of 512 rows x
+    2048 columns (weights ~N(0, 0.02^2), exp_bias -4): blocks encoded per second, with
+    the oracle's search timed on a 64-block sample of the same matrix."""
+    M, K, eb = 512, 2048, -4
+    W = (synth.normal_f32(synth.config_seed(7), "encoder.W", (M, K)) * 0.02).astype(np.float32)
+    Wd = torch.from_numpy(W).cuda()
+    seedmm.search(Wd[:4], P, eb)                      # warm-up (module load, first launch)
+    torch.cuda.synchronize()
+    reps, t = 3, 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        enc = seedmm.search(Wd, P, eb)
+        torch.cuda.synchronize()
+        t += time.perf_counter() - t0
+    t /= reps
+    nblk = M * K // 8
+    res = {"workload": f"exhaustive seed search, fp32 W {M}x{K}, P={P}, exp_bias {eb}",
+           "blocks": nblk, "s_per_matrix": t, "blocks_per_s": nblk / t,
+           "seed_trials_per_s": nblk * 65535 / t,
+           "mean_block_sq_err": float(enc["err"].mean())}
+    if not no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.search_matrix(W[:1, :512], P, eb)      # 64 blocks
+        tc = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": 64 / tc, "unit": "blocks/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": "oracle search of the first 64 blocks of the matrix"}
+    return res
 
 
 def main():
@@ -300,6 +335,9 @@ def main():
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
                               "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6}
         out["by_batch"] = sweep
+
+    if not args.no_encoder:
+        out["encoder"] = encoder_bench(torch, seedmm, synth, P, args.no_cpu)
 
     if not args.no_cpu:
         import oracle
