@@ -58,6 +58,7 @@ def lib():
         L.seedref_expert_accum.argtypes = [p, p, p, i32, p, p, p, i32, p, p, p, i32,
                                            p, f64, p, i32, i32, i32]
         L.seedref_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32] + [p] * 12
+        L.seedref_moe_mixed.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, p] + [p] * 12
         L.seedref_search_block.argtypes = [p, i32, i32, p, p, p, p]
         L.seedref_search_block_w.argtypes = [p, p, i32, i32, p, p, p, p]
         L.seedref_search_matrix.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p]
@@ -184,6 +185,25 @@ def moe(topk_ids: np.ndarray, topk_w: np.ndarray, x: np.ndarray, E: int, H: int,
                  _ptr(np.ascontiguousarray(m["codes"])),
                  _ptr(np.ascontiguousarray(m["exp_bias"], dtype=np.int32))]
     _check(lib().seedref_moe(_ptr(ids), _ptr(w), T, k, _ptr(x), _ptr(y), E, H, I, P, *args), "moe")
+    return y
+
+
+def moe_mixed(topk_ids: np.ndarray, topk_w: np.ndarray, x: np.ndarray, E: int, H: int, I: int,
+              Pe, gate: dict, up: dict, down: dict) -> np.ndarray:
+    """The routed layer with P chosen per expert (Pe: E values, 3 or 4)."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    T, k = ids.shape
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(T, H)
+    y = np.zeros((T, H), dtype=np.float32)
+    pe = np.ascontiguousarray(Pe, dtype=np.int32)
+    args = []
+    for m in (gate, up, down):
+        args += [_ptr(np.ascontiguousarray(m["seeds"])), _ptr(np.ascontiguousarray(m["coefs"])),
+                 _ptr(np.ascontiguousarray(m["codes"])),
+                 _ptr(np.ascontiguousarray(m["exp_bias"], dtype=np.int32))]
+    _check(lib().seedref_moe_mixed(_ptr(ids), _ptr(w), T, k, _ptr(x), _ptr(y), E, H, I, _ptr(pe),
+                                   *args), "moe_mixed")
     return y
 
 

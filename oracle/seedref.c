@@ -277,6 +277,54 @@ int seedref_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
     return 0;
 }
 
+/* Mixed packs ([K2CARD "This upload"] and the pages' hybrid packs: P chosen per
+ * expert): expert e has P_e coefficients per block; its seed and code streams sit at the
+ * same strides as in seedref_moe, its coefficient stream follows the streams of experts
+ * 0..e-1, i.e. at word sum_{e' < e} nblk * P_e' / 4. */
+int seedref_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                      const float *x, float *y, int E, int H, int I, const int32_t *Pe,
+                      const uint16_t *g_seeds, const uint16_t *g_coefs, const uint8_t *g_codes, const int32_t *g_eb,
+                      const uint16_t *u_seeds, const uint16_t *u_coefs, const uint8_t *u_codes, const int32_t *u_eb,
+                      const uint16_t *d_seeds, const uint16_t *d_coefs, const uint8_t *d_codes, const int32_t *d_eb)
+{
+    if (T < 0 || top_k < 1 || E < 1)
+        return -1;
+    for (int e = 0; e < E; ++e)
+        if (bad_args(I, H, Pe[e]) || bad_args(H, I, Pe[e]))
+            return -1;
+    for (int64_t n = 0; n < (int64_t)T * top_k; ++n)
+        if (topk_ids[n] < 0 || topk_ids[n] >= E)
+            return -1;
+    int64_t nblk = (int64_t)I * (H / 8);
+    int64_t code_bytes = nblk / 2;
+    if (nblk % 4 != 0)
+        return -1;
+    int64_t *coff = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t off = 0;
+    for (int e = 0; e < E; ++e) {
+        coff[e] = off;
+        off += nblk * Pe[e] / 4;
+    }
+    double *acc = (double *)malloc(sizeof(double) * (size_t)(H > 0 ? H : 1));
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < H; ++k)
+            acc[k] = 0.0;
+        for (int s = 0; s < top_k; ++s) {
+            int e = topk_ids[(int64_t)t * top_k + s];
+            double wgt = (double)topk_w[(int64_t)t * top_k + s];
+            seedref_expert_accum(g_seeds + e * nblk, g_coefs + coff[e], g_codes + e * code_bytes, g_eb[e],
+                                 u_seeds + e * nblk, u_coefs + coff[e], u_codes + e * code_bytes, u_eb[e],
+                                 d_seeds + e * nblk, d_coefs + coff[e], d_codes + e * code_bytes, d_eb[e],
+                                 x + (int64_t)t * H, wgt, acc, H, I, Pe[e]);
+        }
+        for (int k = 0; k < H; ++k)
+            y[(int64_t)t * H + k] = (float)acc[k];
+    }
+    free(acc);
+    free(coff);
+    return 0;
+}
+
 /* Solve the P x P system a x = r by Gaussian elimination with partial pivoting. */
 static int solve_small(double a[4][4], double r[4], int P, double x[4])
 {

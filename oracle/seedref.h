@@ -86,6 +86,15 @@ int seedref_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
                 const uint16_t *u_seeds, const uint16_t *u_coefs, const uint8_t *u_codes, const int32_t *u_eb,
                 const uint16_t *d_seeds, const uint16_t *d_coefs, const uint8_t *d_codes, const int32_t *d_eb);
 
+/* The same layer with P chosen per expert (Pe[E], 3 or 4; nblk % 4 == 0): seed and code
+ * streams at the uniform strides, expert e's coefficient words after those of experts
+ * 0..e-1 (word offset sum_{e' < e} nblk * Pe[e'] / 4). */
+int seedref_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                      const float *x, float *y, int E, int H, int I, const int32_t *Pe,
+                      const uint16_t *g_seeds, const uint16_t *g_coefs, const uint8_t *g_codes, const int32_t *g_eb,
+                      const uint16_t *u_seeds, const uint16_t *u_coefs, const uint8_t *u_codes, const int32_t *u_eb,
+                      const uint16_t *d_seeds, const uint16_t *d_coefs, const uint8_t *d_codes, const int32_t *d_eb);
+
 /* Exhaustive seed search for one block (the encoder's inner step, unweighted).
  * For every seed 1..65535: least-squares coefficients in double, then for every code
  * 0..15 round-half-even / clamp to [-8,7] and measure the exact squared error; keeps

@@ -85,6 +85,17 @@ def seed_matrix(base: int, tag: str, M: int, K: int, P: int, E: int = 1, exp_bia
     return {"seeds": seeds, "coefs": coefs, "codes": codes, "exp_bias": eb}
 
 
+def seed_matrix_mixed(base: int, tag: str, M: int, K: int, Ps, exp_bias: int = -4):
+    """Random streams for len(Ps) stacked [M][K] matrices, matrix e with Ps[e] coefficients
+    per block: each matrix generated on its own sub-stream, the streams concatenated in
+    matrix order (requires (M*K/8) % 4 == 0).  Also returns 'P' (int32[E])."""
+    assert (M * (K // 8)) % 4 == 0
+    parts = [seed_matrix(base, f"{tag}.m{e}", M, K, int(P), 1, exp_bias) for e, P in enumerate(Ps)]
+    out = {k: np.concatenate([p_[k] for p_ in parts]) for k in ("seeds", "coefs", "codes", "exp_bias")}
+    out["P"] = np.asarray(Ps, dtype=np.int32)
+    return out
+
+
 def normal_f32(base: int, tag: str, shape) -> np.ndarray:
     """N(0,1) samples by Box-Muller in float64, rounded to fp32."""
     n = int(np.prod(shape))

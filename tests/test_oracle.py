@@ -455,3 +455,43 @@ def test_search_matrix_round_trips_a_seed_coded_matrix(oracle, P):
     enc = oracle.search_matrix(W, P, -4)
     np.testing.assert_array_equal(enc["err"], 0.0)
     np.testing.assert_array_equal(oracle.reconstruct_f32(enc, M, K, P), W)
+
+
+def _mixed_layer(E, H, I, Ps, tag):
+    base = synth.config_seed(10)
+    return tuple(synth.seed_matrix_mixed(base, f"{tag}.{n}", *((I, H) if n != "down" else (H, I)), Ps)
+                 for n in ("gate", "up", "down"))
+
+
+def test_moe_mixed_with_one_p_is_the_uniform_layer(oracle):
+    E, H, I, T, k = 4, 64, 32, 3, 2
+    for P in (4, 3):
+        base = synth.config_seed(10)
+        mats = [synth.seed_matrix(base, f"u{P}.{n}", *((I, H) if n != "down" else (H, I)), P, E)
+                for n in ("gate", "up", "down")]
+        ids, w = synth.route_topk(base, f"u{P}.r", T, E, k)
+        x = synth.normal_f32(base, f"u{P}.x", (T, H))
+        np.testing.assert_array_equal(oracle.moe_mixed(ids, w, x, E, H, I, [P] * E, *mats),
+                                      oracle.moe(ids, w, x, E, H, I, P, *mats))
+
+
+def test_moe_mixed_is_the_slot_sum_of_each_experts_own_ffn(oracle):
+    # a stack of P3 and P4 experts: every token's output is the weighted slot sum of the
+    # single-expert FFNs, each expert read from its own (un-stacked) streams with its own P
+    E, H, I, T, k = 5, 64, 32, 4, 3
+    Ps = [4, 3, 3, 4, 3]
+    base = synth.config_seed(10)
+    parts = {n: [synth.seed_matrix(base, f"mx.{n}.m{e}", *((I, H) if n != "down" else (H, I)), Ps[e])
+                 for e in range(E)] for n in ("gate", "up", "down")}
+    stacked = [synth.seed_matrix_mixed(base, f"mx.{n}", *((I, H) if n != "down" else (H, I)), Ps)
+               for n in ("gate", "up", "down")]
+    ids, w = synth.route_topk(base, "mx.r", T, E, k)
+    x = synth.normal_f32(base, "mx.x", (T, H))
+    y = oracle.moe_mixed(ids, w, x, E, H, I, Ps, *stacked)
+    for t in range(T):
+        ref = np.zeros(H)
+        for s in range(k):
+            e = int(ids[t, s])
+            ref += float(w[t, s]) * oracle.expert(parts["gate"][e], parts["up"][e], parts["down"][e],
+                                                  x[t:t + 1], H, I, Ps[e])[0].astype(np.float64)
+        np.testing.assert_allclose(y[t], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
