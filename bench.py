@@ -55,6 +55,8 @@ def parse():
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--no-encoder", action="store_true",
                     help="skip the seed-search (encoder) measurement")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="skip the mixed P3/P4 layer measurement")
     return ap.parse_args()
 
 
@@ -118,6 +120,64 @@ class HipEvents:
         for h in self.live:
             self.hip.hipEventDestroy(self.ct.c_void_p(h))
         self.live = []
+
+
+def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, steps=30):
+    """The same layer as a mixed pack: a seeded random half of the experts P = 4, the
+    rest P = 3 (seedmm_moe_mixed); HIP-graph replays over six input sets and the weight
+    replicas, as for the headline step."""
+    base = synth.config_seed(11)
+    Ps = [4 if v else 3 for v in (synth.uniform_u64(base, "mix.P", E) & np.uint64(1))]
+    host = {n: synth.seed_matrix_mixed(base, f"mix.{n}", *((I, H) if n != "down" else (H, I)), Ps)
+            for n in ("gate", "up", "down")}
+    reps = [{n: to_dev(m) for n, m in host.items()}]
+    for _ in range(replicas - 1):
+        reps.append({n: {k: v.clone() for k, v in m.items()} for n, m in reps[0].items()})
+    mask = seedmm.p4_mask(Ps, dev)
+    ids_l, w_l, x_l, dist = [], [], [], []
+    for g in range(6):
+        i, w = synth.route_topk(base, f"mix.r{g}", T, E, TOPK)
+        x = synth.bf16_bits(synth.normal_f32(base, f"mix.x{g}", (T, H)))
+        ids_l.append(torch.from_numpy(i).to(dev)), w_l.append(torch.from_numpy(w).to(dev))
+        x_l.append(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev))
+        dist.append(np.unique(i))
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(seedmm.moe_workspace_bytes(T, TOPK, E, H, I), dtype=torch.uint8, device=dev)
+
+    def call(g):
+        r = reps[g % len(reps)]
+        seedmm.moe_mixed(ids_l[g], w_l[g], x_l[g], E, H, I, mask, r["gate"], r["up"], r["down"],
+                         y=y, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for g in range(6):
+            call(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for g in range(6):
+        G = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(G):
+            call(g)
+        graphs.append(G)
+    for s_ in range(6):
+        graphs[s_].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        graphs[s_ % 6].replay()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    nblk = H * I // 8
+    wts = np.mean([len(d) for d in dist]) * 3 * H * I
+    cb = np.mean([sum(3 * (nblk * 2 + nblk * Ps[e] // 4 * 2 + nblk // 2) for e in d) for d in dist])
+    return {"workload": f"moe_layer_decode, mixed pack ({sum(p == 4 for p in Ps)} P4 / "
+                        f"{sum(p == 3 for p in Ps)} P3 experts), T={T}",
+            "bits_per_weight": float(np.mean([16 + 4 * p + 4 for p in Ps]) / 8),
+            "ms_per_step": t * 1e3, "weights_per_s": wts / t, "compressed_GBps": cb / t / 1e9,
+            "tok_s": T / t}
 
 
 def encoder_bench(torch, seedmm, synth, P, no_cpu):
@@ -335,6 +395,9 @@ def main():
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
                               "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6}
         out["by_batch"] = sweep
+
+    if not args.no_mixed:
+        out["mixed"] = mixed_bench(torch, seedmm, synth, dev, T, args.replicas, to_dev)
 
     if not args.no_encoder:
         out["encoder"] = encoder_bench(torch, seedmm, synth, P, args.no_cpu)

@@ -162,6 +162,24 @@ int seedmm_moe_timed(const int32_t *topk_ids, const float *topk_w, int T, int to
                      void *const *events);
 
 /*
+ * seedmm_moe_mixed -- seedmm_moe for mixed packs: P chosen per expert (NanoSeedLM
+ * documentation index: "Results", hybrid P3 / P4 seed packs with a third of the experts
+ * in P4; "Plans", a P4 tier for the hot experts and P3 for the rest).
+ *   p4mask: device uint32[ceil(E/32)], bit e (word e/32, bit e%32) set when expert e has
+ *   P = 4, clear when it has P = 3.
+ *   Stacked streams: seeds and codes at the same per-expert strides as seedmm_moe;
+ *   expert e's coefficient stream starts at word (I*H/8/4) * (3e + number of P = 4
+ *   experts before e), i.e. the experts' own streams concatenated in expert order.
+ *   Requires (I*H/8) % 4 == 0.  Other arguments, results and errors as seedmm_moe
+ *   (SEEDMM_EINVAL also for a NULL p4mask).  Each expert kernel runs once per P; a
+ *   launch serves only the experts of its P.
+ */
+int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                     const void *x, float *y, int E, int H, int I, const uint32_t *p4mask,
+                     seedmm_mat gate, seedmm_mat up, seedmm_mat down,
+                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * seedmm_search -- encode W [M][K] into a seed-coded matrix by the exhaustive seed search
  * (Qwen3.8-Flash-Next-NanoSeedLM-P4 card, "How it works": every one of the 65,535 seeds
  * is tried for every block; barnson.org post, "GPU search == CPU search").  For each

@@ -12,6 +12,7 @@
  *   [BLOG]    barnson.org post on NanoSeedLM, sections "Where this started",
  *             "What I changed: September 2026", "LFSR is free", "Four bits is four bits",
  *             "GPU search == CPU search".
+ *   [INDEX]   NanoSeedLM documentation index page, sections "Results" and "Plans".
  *
  * Build: cc -O2 -std=c99 -ffp-contract=off -fopenmp -shared -fPIC seedref.c -lm
  */
@@ -277,8 +278,9 @@ int seedref_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
     return 0;
 }
 
-/* Mixed packs ([K2CARD "This upload"] and the pages' hybrid packs: P chosen per
- * expert): expert e has P_e coefficients per block; its seed and code streams sit at the
+/* Mixed packs, P chosen per expert ([INDEX "Results"]: hybrid P3 / P4 packs with a
+ * third of the experts in P4; [INDEX "Plans"]: hot experts in P4, the rest in P3):
+ * expert e has P_e coefficients per block; its seed and code streams sit at the
  * same strides as in seedref_moe, its coefficient stream follows the streams of experts
  * 0..e-1, i.e. at word sum_{e' < e} nblk * P_e' / 4. */
 int seedref_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,

@@ -117,11 +117,28 @@ struct Mat {
     int exp_bias;
 };
 
+// Mixed packs (P chosen per expert): bit e of p4mask is set when expert e has P = 4.
+__device__ __forceinline__ bool p4_of(const uint32_t* p4mask, int e) {
+    return (p4mask[e >> 5] >> (e & 31)) & 1u;
+}
+
+// Coefficient words of experts 0..e-1: e * nblk * P / 4 for one P; with a mask, experts
+// of P = 3 take 3 nblk / 4 words and experts of P = 4 take nblk words (nblk % 4 == 0).
+__device__ __forceinline__ int64_t coef_words_before(const uint32_t* p4mask, int e,
+                                                     int64_t nblk, int P) {
+    if (!p4mask) return (int64_t)e * (nblk * P / 4);
+    int n4 = 0;
+    for (int w = 0; w < (e >> 5); ++w) n4 += __popc(p4mask[w]);
+    n4 += __popc(p4mask[e >> 5] & ((1u << (e & 31)) - 1u));
+    return (nblk / 4) * (3 * (int64_t)e + n4);
+}
+
 __device__ __forceinline__ Mat mat_of(const seedmm_mat& m, int e, int64_t nblk, int P,
-                                      int eb_scalar, bool eb_from_ptr) {
+                                      int eb_scalar, bool eb_from_ptr,
+                                      const uint32_t* p4mask = nullptr) {
     Mat r;
     r.seeds = m.seeds + (int64_t)e * nblk;
-    r.coefs = m.coefs + (int64_t)e * (nblk * P / 4);
+    r.coefs = m.coefs + coef_words_before(p4mask, e, nblk, P);
     r.codes = m.codes + (int64_t)e * (nblk / 2);
     r.exp_bias = eb_from_ptr ? m.exp_bias[e] : eb_scalar;
     return r;
@@ -278,6 +295,8 @@ struct MfmaArgs {
     uint16_t* h;            // GATEUP: bf16 [T*top_k][ldy]
     int ldy;
     const int32_t* ids;     // one token (T = 1): topk_ids, workgroup y serves slot y
+    const uint32_t* p4mask; // mixed packs: bit e set = expert e has P = 4; this launch
+                            // serves the experts of its own P only (null: one P)
 };
 
 // Pair lists of the one-token path: slot y's list is the single pair index y.
@@ -418,57 +437,21 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
 
 // 4 waves on 16 weight rows.  GATEUP: waves 0-1 regenerate gate, waves 2-3 up, each
 // over half of K; otherwise the 4 waves take a quarter of K each.
+// The products of one workgroup once its expert (e, n_e pairs in `list`) is known.
 template <int P, bool VEC, int NT, int MODE, bool TAB, int RT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2))) void k_mfma(const MfmaArgs a) {
-    static_assert(MODE != MODE_GATEUP || RT == 1, "gate/up pairs its waves by matrix");
+__device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, const int32_t* list,
+                                         const uint32_t* tab, f32x4 (*red)[NT][64]) {
     constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;
-    __shared__ f32x4 red[4][NT][64];
-    __shared__ uint32_t tab[TAB ? 512 : 1];
-    if constexpr (TAB) fill_lfsr_tables(tab);
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15;
-
-    // ---- which expert this workgroup serves --------------------------------------
-    int e = 0, n_e = a.N;
-    const int32_t* list = nullptr;
-    if (MODE != MODE_GEMM && a.ids) {
-        // one token: its top_k slots are top_k distinct experts, one workgroup row each
-        e = a.ids[blockIdx.y];
-        if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
-        n_e = 1;
-        list = kSlotIota + blockIdx.y;
-    } else if constexpr (MODE != MODE_GEMM) {
-        const int target = blockIdx.y;
-        int found = -1, cum = 0;
-        for (int base = 0; base < a.E && found < 0; base += 64) {
-            const int idx = base + lane;
-            const bool act = idx < a.E && a.counts[idx] > 0;
-            const uint64_t bal = __ballot(act);
-            const int c = __popcll(bal);
-            if (target < cum + c) {
-                const int k = target - cum;
-                const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
-                const bool mine = act && __popcll(below) == k;
-                found = base + __ffsll((long long)__ballot(mine)) - 1;
-            }
-            cum += c;
-        }
-        if (found < 0) return;   // uniform across the workgroup
-        e = found;
-        n_e = a.counts[e];
-        list = a.lists + (int64_t)e * a.T;
-    }
-    if (n_e <= 0) return;
-
     Lane L;
     L.tab = TAB ? tab : nullptr;
     L.ks = wave % KS;
     L.q = lane >> 4;
     L.nbpr = a.K / 8;
     const int64_t nblk = (int64_t)a.M * L.nbpr;
-    if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true);
-    else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
+    if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask);
+    else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask);
     const int m0 = blockIdx.x * 16 * RT;
     const int row = m0 + 16 * (wave / KS % RT) + r;
     L.rv = row < a.M;
@@ -486,6 +469,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2
             default: mfma_pass<P, VEC, 4, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
         }
     }
+}
+
+// Mixed packs (a.p4mask set) run one launch per P; each launch serves only the experts
+// of its own P.  (One launch holding both bodies was slower: the two bodies shared one
+// register allocation and the P = 3 loop came out scheduled worse than in its own kernel.)
+template <int P, bool VEC, int NT, int MODE, bool TAB, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2))) void k_mfma(const MfmaArgs a) {
+    static_assert(MODE != MODE_GATEUP || RT == 1, "gate/up pairs its waves by matrix");
+    __shared__ f32x4 red[4][NT][64];
+    __shared__ uint32_t tab[TAB ? 512 : 1];
+
+    const int lane = threadIdx.x & 63;
+
+    // ---- which expert this workgroup serves --------------------------------------
+    int e = 0, n_e = a.N;
+    const int32_t* list = nullptr;
+    if (MODE != MODE_GEMM && a.ids) {
+        // one token: its top_k slots are top_k distinct experts, one workgroup row each
+        e = a.ids[blockIdx.y];
+        if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
+        if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
+        n_e = 1;
+        list = kSlotIota + blockIdx.y;
+    } else if constexpr (MODE != MODE_GEMM) {
+        // the target-th active expert (of this launch's P when the pack is mixed)
+        const int target = blockIdx.y;
+        int found = -1, cum = 0;
+        for (int base = 0; base < a.E && found < 0; base += 64) {
+            const int idx = base + lane;
+            const bool act = idx < a.E && a.counts[idx] > 0 &&
+                             (!a.p4mask || p4_of(a.p4mask, idx) == (P == 4));
+            const uint64_t bal = __ballot(act);
+            const int c = __popcll(bal);
+            if (target < cum + c) {
+                const int k = target - cum;
+                const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+                const bool mine = act && __popcll(below) == k;
+                found = base + __ffsll((long long)__ballot(mine)) - 1;
+            }
+            cum += c;
+        }
+        if (found < 0) return;   // uniform across the workgroup
+        e = found;
+        n_e = a.counts[e];
+        list = a.lists + (int64_t)e * a.T;
+    }
+    if (n_e <= 0) return;
+    if constexpr (TAB) fill_lfsr_tables(tab);
+    mfma_run<P, VEC, NT, MODE, TAB, RT>(a, e, n_e, list, tab, red);
 }
 
 // ----------------------------------------------------------------------------------
@@ -550,7 +582,8 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
         int found = -1, cum = 0;
         for (int base = 0; base < a.E && found < 0; base += 64) {
             const int idx = base + lane;
-            const bool act = idx < a.E && a.counts[idx] > 0;
+            const bool act = idx < a.E && a.counts[idx] > 0 &&
+                             (!a.p4mask || p4_of(a.p4mask, idx) == (P == 4));
             const uint64_t bal = __ballot(act);
             const int c = __popcll(bal);
             if (target < cum + c) {
@@ -581,9 +614,9 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     // ---- regeneration role: A row `arow` (matrix dmat, row drow), block lane dj ------
     const int arow = tid >> 2, dj = tid & 3;
     const int dmat = arow / RM, drow = arow % RM;
-    Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM);
+    Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask);
     if constexpr (NMAT == 2) {
-        if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true);
+        if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask);
     }
     const bool drv = m0 + drow < M;
     const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
@@ -939,12 +972,15 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     }
 }
 
+// P = 3 or 4, or P = 0 for mixed packs (a.p4mask): then one launch per P, each serving
+// only the experts of its own P.
 template <int MODE>
 void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
-    if (P == 4) {
+    if (P == 0 || P == 4) {
         if (vec) launch_mfma<4, true, MODE>(a, prefill, gridy, st);
         else launch_mfma<4, false, MODE>(a, prefill, gridy, st);
-    } else {
+    }
+    if (P == 0 || P == 3) {
         if (vec) launch_mfma<3, true, MODE>(a, prefill, gridy, st);
         else launch_mfma<3, false, MODE>(a, prefill, gridy, st);
     }
@@ -1064,14 +1100,21 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I) {
     return L.total;
 }
 
-int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int top_k,
-                     const void* x, float* y, int E, int H, int I, int P, seedmm_mat gate,
-                     seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
-                     void* hip_stream, void* const* events) {
+}  // extern "C"
+
+namespace {
+
+// The routed layer; P = 3 or 4 for one P, or P = 0 with p4mask (device, bit e = expert e
+// has P = 4) for mixed packs, whose expert kernels run once per P.
+int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
+            float* y, int E, int H, int I, int P, const uint32_t* p4mask, seedmm_mat gate,
+            seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
+            void* hip_stream, void* const* events) {
     if (T < 0 || E < 1 || E > 4096 || top_k < 1 || top_k > E || top_k > 64) return SEEDMM_EINVAL;
-    if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0 || (P != 3 && P != 4)) return SEEDMM_EINVAL;
+    if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0) return SEEDMM_EINVAL;
+    if (P == 0 ? !p4mask : (P != 3 && P != 4)) return SEEDMM_EINVAL;
     const int64_t nblk = (int64_t)I * (H / 8);   // blocks of one gate/up/down matrix
-    if ((nblk * P) % 4 != 0 || nblk % 2 != 0) return SEEDMM_EINVAL;
+    if (P == 0 ? nblk % 4 != 0 : ((nblk * P) % 4 != 0 || nblk % 2 != 0)) return SEEDMM_EINVAL;
     if (T == 0) return SEEDMM_OK;
     const seedmm_mat* mats[3] = {&gate, &up, &down};
     for (const seedmm_mat* m : mats)
@@ -1105,7 +1148,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     const bool prefill = (int64_t)pairs >= 64LL * E;  // >= 64 tokens per expert on average
     bool vec = true;
     for (const seedmm_mat* m : mats) vec = vec && use_vec(m->seeds, m->coefs, m->codes, 64);
-    vec = vec && H % 64 == 0 && I % 64 == 0 && (nblk % 8 == 0);
+    vec = vec && H % 64 == 0 && I % 64 == 0 && (nblk % 32 == 0);
 
     MfmaArgs a = {};
     a.A = gate; a.A2 = up;
@@ -1114,6 +1157,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     a.counts = counts; a.lists = lists; a.E = E; a.T = T; a.top_k = top_k;
     a.h = hbuf; a.ldy = I;
     a.ids = one ? topk_ids : nullptr;
+    a.p4mask = p4mask;
     mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
     mark(2);
 
@@ -1124,6 +1168,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
     b.counts = counts; b.lists = lists; b.E = E; b.T = T; b.top_k = top_k;
     b.topk_w = topk_w; b.y = obuf; b.ldy = H;
     b.ids = a.ids;
+    b.p4mask = p4mask;
     mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
     mark(3);
 
@@ -1132,6 +1177,28 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
                        top_k, y, H, T);
     mark(4);
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int top_k,
+                     const void* x, float* y, int E, int H, int I, int P, seedmm_mat gate,
+                     seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
+                     void* hip_stream, void* const* events) {
+    if (P != 3 && P != 4) return SEEDMM_EINVAL;
+    return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, P, nullptr, gate, up, down,
+                   workspace, workspace_bytes, hip_stream, events);
+}
+
+int seedmm_moe_mixed(const int32_t* topk_ids, const float* topk_w, int T, int top_k,
+                     const void* x, float* y, int E, int H, int I, const uint32_t* p4mask,
+                     seedmm_mat gate, seedmm_mat up, seedmm_mat down, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+    if (!p4mask) return SEEDMM_EINVAL;
+    return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, 0, p4mask, gate, up, down,
+                   workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,

@@ -47,11 +47,13 @@ def _load():
                              p, ctypes.c_size_t, p]
     L.seedmm_moe_timed.argtypes = L.seedmm_moe.argtypes + [p]
     L.seedmm_search.argtypes = [p, i32, p, i32, i32, i32, ctypes.c_int32, p, p, p, p, p]
+    L.seedmm_moe_mixed.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, p, SeedMat, SeedMat,
+                                   SeedMat, p, ctypes.c_size_t, p]
     L.seedmm_strerror.restype = ctypes.c_char_p
     L.seedmm_strerror.argtypes = [i32]
     L.seedmm_version.restype = i32
     for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-                 "seedmm_moe", "seedmm_moe_timed", "seedmm_search"):
+                 "seedmm_moe", "seedmm_moe_timed", "seedmm_search", "seedmm_moe_mixed"):
         getattr(L, name).restype = i32
     return L
 
@@ -59,8 +61,8 @@ def _load():
 _lib = _load()
 
 EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_search",
-           "seedmm_strerror", "seedmm_version")
+           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_mixed",
+           "seedmm_search", "seedmm_strerror", "seedmm_version")
 
 
 def lib():
@@ -194,6 +196,41 @@ def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None,
     else:
         arr = (ctypes.c_void_p * 5)(*[getattr(ev, "cuda_event", ev) for ev in events])
         _check(_lib.seedmm_moe_timed(*args, arr), "seedmm_moe_timed")
+    return y
+
+
+def p4_mask(Ps, device) -> torch.Tensor:
+    """Device bitmask of the experts with P = 4 (bit e of word e // 32)."""
+    E = len(Ps)
+    words = [0] * ((E + 31) // 32)
+    for e, P in enumerate(Ps):
+        if int(P) == 4:
+            words[e >> 5] |= 1 << (e & 31)
+        elif int(P) != 3:
+            raise ValueError("every expert's P must be 3 or 4")
+    return torch.tensor([w - (1 << 32) if w >= (1 << 31) else w for w in words],
+                        dtype=torch.int32, device=device)
+
+
+def moe_mixed(topk_ids, topk_w, x, E, H, I, p4mask, gate, up, down, y=None, workspace=None,
+              stream=None):
+    """Routed SwiGLU MoE layer with P chosen per expert (seedmm_moe_mixed); p4mask from
+    p4_mask()."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float32, "topk_w")
+    _dev(x, torch.bfloat16, "x")
+    _dev(p4mask, torch.int32, "p4mask")
+    T, k = topk_ids.shape
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+                                device=x.device)
+    _check(_lib.seedmm_moe_mixed(_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I,
+                                 _ptr(p4mask), _seedmat(gate), _seedmat(up), _seedmat(down),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "seedmm_moe_mixed")
     return y
 
 

@@ -128,3 +128,10 @@ def test_search_rejects(lib):
     assert f(None, 16, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, None) == -1    # null W
     assert f(FAKE, 16, None, 4, 16, 4, -4, FAKE, None, FAKE, None, None) == -1    # null coefs
     assert f(None, 16, None, 0, 16, 4, -4, None, None, None, None, None) == 0     # empty
+
+
+def test_moe_mixed_rejects_a_missing_mask(lib):
+    from pseudo_random_weight_amd.seedmm import SeedMat
+    m = SeedMat(FAKE, FAKE, FAKE, FAKE)
+    assert lib.seedmm_moe_mixed(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 64, 64, None, m, m, m,
+                                FAKE, 1 << 30, None) == -1

@@ -418,3 +418,66 @@ def test_search_recovers_a_seed_coded_matrix(sm, oracle, P):
     Wg = sm.reconstruct(got, M, K, P)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(Wg.cpu().numpy(), W)
+
+
+# ---------------------------------------------------------------------------------
+# Mixed packs: P chosen per expert
+# ---------------------------------------------------------------------------------
+def _mixed(E, H, I, Ps, tag):
+    base = synth.config_seed(10)
+    return tuple(synth.seed_matrix_mixed(base, f"{tag}.{n}", *((I, H) if n != "down" else (H, I)), Ps)
+                 for n in ("gate", "up", "down"))
+
+
+def _run_mixed(sm, mats, Ps, ids, w, x, E, H, I):
+    import torch
+    xt, x32 = bf16_tensor(x)
+    mask = sm.p4_mask(Ps, "cuda")
+    y = sm.moe_mixed(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), xt, E, H, I, mask,
+                     *[dev(m) for m in mats])
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), x32
+
+
+@pytest.mark.parametrize("T", [1, 5, 600])
+def test_moe_mixed_matches_oracle(sm, oracle, T):
+    """P3 and P4 experts in one stack: decode (T = 5), one token (T = 1) and the prefill
+    path (T = 600, 150 tokens per expert) against the oracle's mixed layer."""
+    E, H, I, k = 8, 256, 128, 2
+    Ps = [4, 3, 3, 4, 3, 4, 4, 3]
+    say("moe mixed", T)
+    mats = _mixed(E, H, I, Ps, "mxg")
+    base = synth.config_seed(10)
+    ids, w = synth.route_topk(base, f"mxg.r{T}", T, E, k)
+    x = synth.normal_f32(base, f"mxg.x{T}", (T, H))
+    y, x32 = _run_mixed(sm, mats, Ps, ids, w, x, E, H, I)
+    rows = range(T) if T <= 8 else (0, 17, T // 2, T - 1)
+    for t in rows:
+        ref = oracle.moe_mixed(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, Ps, *mats)
+        assert rel_l2(y[t], ref[0]) <= 1e-2, t
+
+
+def test_moe_mixed_full_size_sampled(sm, oracle):
+    E, H, I, k, T = 100, 2048, 1024, 8, 16
+    Ps = [4 if v else 3 for v in (synth.uniform_u64(synth.config_seed(10), "mix.P", E) & np.uint64(1))]
+    say("moe mixed full size", sum(p == 4 for p in Ps))
+    mats = _mixed(E, H, I, Ps, "mxf")
+    base = synth.config_seed(10)
+    ids, w = synth.route_topk(base, "mxf.r", T, E, k)
+    x = synth.normal_f32(base, "mxf.x", (T, H))
+    y, x32 = _run_mixed(sm, mats, Ps, ids, w, x, E, H, I)
+    for t in (0, 9, 15):
+        ref = oracle.moe_mixed(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, Ps, *mats)
+        assert rel_l2(y[t], ref[0]) <= 1e-2, t
+
+
+@pytest.mark.parametrize("P,T", [(4, 16), (3, 16), (3, 1)])
+def test_moe_mixed_with_one_p_is_the_uniform_layer(sm, P, T):
+    """A mixed pack whose experts all have one P is that P's uniform pack: bit-identical
+    outputs from the mixed entry point and the uniform one."""
+    E, H, I, k = 100, 2048, 1024, 8
+    say("moe mixed all-P vs uniform", P, T)
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2, f"mxu{P}")
+    y_uni, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    y_mix, _ = _run_mixed(sm, (gate, up, down), [P] * E, ids, w, x, E, H, I)
+    assert np.array_equal(y_uni.view(np.uint32), y_mix.view(np.uint32))
