@@ -60,6 +60,21 @@ def parse():
     return ap.parse_args()
 
 
+def host_cpu():
+    """CPU model and the cores this process may use (for the oracle baseline)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "nproc": len(os.sched_getaffinity(0)),
+            "logical_cpus": os.cpu_count()}
+
+
 def compressed_bytes_per_matrix(P):
     nblk = H * I // 8
     return nblk * 2 + (nblk * P + 3) // 4 * 2 + (nblk + 1) // 2
@@ -298,16 +313,22 @@ def main():
 
     NB = 6   # input sets cycled by the graph replays (each paired with replica g % replicas)
 
-    def run_graph(T, warmup, steps):
+    def run_graph(T, warmup, steps, nrep=None):
         """Per-step time of HIP-graph replays: one graph per input set captures the whole
-        layer call (dispatch, gate/up, down, combine), as a serving loop would."""
+        layer call (dispatch, gate/up, down, combine), as a serving loop would.  Returns
+        the wall time per step (the timed region is bracketed by synchronizations), the
+        distinct experts of each step and the 10th / 50th / 90th percentile of the
+        per-replay times from events recorded between replays in a second, untimed pass
+        (the events add a few microseconds per step).  nrep limits the weight
+        replicas cycled (1: the same weights every step, a hot-cache figure)."""
+        nrep = nrep or len(reps)
         ids_d, w_d, x_d, ids_h = make_batches(T, NB)
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
         ws = torch.empty(seedmm.moe_workspace_bytes(T, TOPK, E, H, I), dtype=torch.uint8,
                          device=dev)
 
         def call(g):
-            r = reps[g % len(reps)]
+            r = reps[g % nrep]
             seedmm.moe(ids_d[g], w_d[g], x_d[g], E, H, I, P, r["gate"], r["up"], r["down"],
                        y=y, workspace=ws)
 
@@ -332,17 +353,27 @@ def main():
             graphs[s_ % NB].replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # per-replay spread from a second pass with an event between replays (events add
+        # a few microseconds per step, so they stay out of the timed region above)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for s_ in range(steps):
+            evs[s_].record()
+            graphs[s_ % NB].replay()
+        evs[steps].record()
+        torch.cuda.synchronize()
+        per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
         distinct = np.array([len(np.unique(ids_h[s_ % NB])) for s_ in range(steps)], dtype=np.float64)
         del graphs
-        return wall / steps, distinct
+        return wall / steps, distinct, np.percentile(per, [10, 50, 90])
 
     # stage times and the roofline come from eager launches with HIP events around each
     # kernel; the step time is HIP-graph replays unless --eager
     t_eager, stages, distinct, ids_h, x_d, w_d = run(T, args.warmup, args.steps)
+    pct = None
     if args.eager:
         t_step = t_eager
     else:
-        t_step, distinct = run_graph(T, args.warmup, args.steps)
+        t_step, distinct, pct = run_graph(T, args.warmup, args.steps)
     w_per_mat = H * I
     weights = distinct.mean() * 3 * w_per_mat
     cbytes = distinct.mean() * 3 * compressed_bytes_per_matrix(P)
@@ -381,6 +412,15 @@ def main():
         "ms_per_step_eager": t_eager * 1e3,
         "roofline": roofline,
     }
+    if pct is not None:
+        out["step_ms_p10_p50_p90"] = [float(v) for v in pct]
+        # the same graphs over a single weight copy: part of the layer stays in the
+        # 256 MB last-level cache between steps (labelled, not the headline)
+        t_hot, dis_hot, pct_hot = run_graph(T, args.warmup, args.steps, nrep=1)
+        out["hot_cache"] = {"ms_per_step": t_hot * 1e3,
+                            "weights_per_s": dis_hot.mean() * 3 * w_per_mat / t_hot,
+                            "step_ms_p10_p50_p90": [float(v) for v in pct_hot],
+                            "note": "one weight copy reused every step"}
 
     if not args.no_sweep:
         sweep = {}
@@ -389,7 +429,7 @@ def main():
                 continue
             ts, st, dis, *_ = run(Ts, 3, 20)
             if not args.eager:
-                ts, dis = run_graph(Ts, 3, 50)
+                ts, dis, _ = run_graph(Ts, 3, 50)
             sweep[str(Ts)] = {"ms_per_step": ts * 1e3, "tok_s": Ts / ts,
                               "weights_per_s": dis.mean() * 3 * w_per_mat / ts,
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
@@ -415,13 +455,28 @@ def main():
                        host["gate"], host["up"], host["down"])
             n += 1
         t_cpu = (time.perf_counter() - t0) / n * T       # the oracle's cost is linear in tokens
+        t_span = time.perf_counter() - t0
         d0 = len(np.unique(ids0))
+        # the same oracle on one thread, over a few tokens
+        threads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t1 = time.perf_counter()
+        n1 = 0
+        while n1 < T and (time.perf_counter() - t1) < args.cpu_seconds / 3:
+            oracle.moe(ids0[n1:n1 + 1], w0[n1:n1 + 1], x0[n1:n1 + 1], E, H, I, P,
+                       host["gate"], host["up"], host["down"])
+            n1 += 1
+        t_cpu1 = (time.perf_counter() - t1) / n1 * T
+        oracle.set_num_threads(threads)
         out["cpu_baseline"] = {
             "value": d0 * 3 * w_per_mat / t_cpu, "unit": "weights/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": f"oracle MoE on the first {n} of the {T} tokens of one step "
-                      f"({time.perf_counter() - t0:.1f} s), scaled linearly to the step",
-            "tok_s": T / t_cpu}
+                      f"({t_span:.1f} s), scaled linearly to the step",
+            "tok_s": T / t_cpu,
+            "single_thread": {"value": d0 * 3 * w_per_mat / t_cpu1, "tok_s": T / t_cpu1,
+                              "sample": f"first {n1} tokens of the same step, one thread"},
+            "host": host_cpu()}
     print(json.dumps(out), flush=True)
 
 

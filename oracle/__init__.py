@@ -63,6 +63,8 @@ def lib():
         L.seedref_search_block_w.argtypes = [p, p, i32, i32, p, p, p, p]
         L.seedref_search_matrix.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p]
         L.seedref_num_threads.restype = ctypes.c_int
+        L.seedref_set_num_threads.restype = None
+        L.seedref_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -246,3 +248,8 @@ def search_matrix(W: np.ndarray, P: int, exp_bias: int, colw: np.ndarray = None)
 
 def num_threads() -> int:
     return int(lib().seedref_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops (results do not depend on it)."""
+    lib().seedref_set_num_threads(int(n))

@@ -495,3 +495,15 @@ int seedref_num_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the parallel loops that follow (timing only; results do not depend on
+ * it, every row is summed in a fixed order). */
+void seedref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -117,6 +117,7 @@ int seedref_search_matrix(const float *W, const float *colw, int M, int K, int P
 
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int seedref_num_threads(void);
+void seedref_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

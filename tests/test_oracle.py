@@ -331,6 +331,21 @@ def test_moe_token_permutation_equivariance(oracle):
     np.testing.assert_array_equal(yp, y[perm])
 
 
+def test_moe_does_not_depend_on_the_thread_count(oracle):
+    """Every row is summed in a fixed order, so the oracle's result is the same on one
+    thread as on many (the benchmark times it both ways)."""
+    E, H, I, T, k = 6, 128, 64, 9, 3
+    gate, up, down, x, ids, w = _small_moe(4, E, H, I, T, k)
+    n = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        y1 = oracle.moe(ids, w, x, E, H, I, 4, gate, up, down)
+    finally:
+        oracle.set_num_threads(n)
+    yn = oracle.moe(ids, w, x, E, H, I, 4, gate, up, down)
+    np.testing.assert_array_equal(y1, yn)
+
+
 def test_moe_rejects_out_of_range_ids(oracle):
     E, H, I, T, k = 3, 64, 32, 2, 1
     gate, up, down, x, _, _ = _small_moe(4, E, H, I, T, k)
