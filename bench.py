@@ -55,6 +55,8 @@ def parse():
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--no-encoder", action="store_true",
                     help="skip the seed-search (encoder) measurement")
+    ap.add_argument("--no-cache", action="store_true",
+                    help="skip the host-resident experts with a device expert cache")
     ap.add_argument("--no-mixed", action="store_true",
                     help="skip the mixed P3/P4 layer measurement")
     return ap.parse_args()
@@ -193,6 +195,79 @@ def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, steps=30):
             "bits_per_weight": float(np.mean([16 + 4 * p + 4 for p in Ps]) / 8),
             "ms_per_step": t * 1e3, "weights_per_s": wts / t, "compressed_GBps": cb / t / 1e9,
             "tok_s": T / t}
+
+
+def cache_bench(torch, seedmm, synth, host, P, steps=200, warmup=30, S=33):
+    """Experts in pinned host memory behind an S-slot device cache (seedmm_cache_moe),
+    one-token decode, eager calls (the cache plans each call on the host).  Two routing
+    recipes: i.i.d. router logits, and a hot third of the experts taking ~85% of the
+    router choices.  Also the host-to-device rate of one large pinned copy."""
+    dev = torch.device("cuda:0")
+    base = synth.config_seed(13)
+    cache = seedmm.ExpertCache(host, E, H, I, P, S)
+    y = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(seedmm.moe_workspace_bytes(1, TOPK, E, H, I), dtype=torch.uint8, device=dev)
+    out = {"workload": f"moe_layer_decode T=1, experts in pinned host memory, {S} of {E} "
+                       f"experts cached on the device (LRU)",
+           "slots": S, "slot_MB": 3 * compressed_bytes_per_matrix(P) / 1e6}
+    hb, _ = synth.hot_bias(base, E)
+    for name, bias in (("uniform", None), ("hot_third", hb)):
+        n = warmup + steps
+        ids, w = synth.route_topk(base, f"cache.{name}", n, E, TOPK, bias=bias)
+        x = synth.bf16_bits(synth.normal_f32(base, f"cache.x.{name}", (n, H)))
+        ids_d = torch.from_numpy(ids).to(dev)
+        w_d = torch.from_numpy(w).to(dev)
+        x_d = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        cache.reset()
+
+        def call(s):
+            cache.moe(ids[s:s + 1], ids_d[s:s + 1], w_d[s:s + 1], x_d[s:s + 1], y=y,
+                      workspace=ws)
+
+        for s in range(warmup):
+            call(s)
+        torch.cuda.synchronize()
+        st0 = cache.stats()
+        t0 = time.perf_counter()
+        for s in range(warmup, n):
+            call(s)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / steps
+        st1 = cache.stats()
+        d = {k: st1[k] - st0[k] for k in st1}
+        out[name] = {"ms_per_step": t * 1e3, "tok_s": 1.0 / t,
+                     "hit_rate": d["hits"] / max(d["uses"], 1),
+                     "loads_per_step": d["misses"] / steps,
+                     "h2d_GBps": d["bytes"] / steps / t / 1e9}
+    # the same one-token calls with every expert resident (eager, for comparison)
+    devm = {}
+    for nme, m in host.items():
+        devm[nme] = {"seeds": torch.from_numpy(m["seeds"].view(np.int16)).view(torch.uint16).to(dev),
+                     "coefs": torch.from_numpy(m["coefs"].view(np.int16)).view(torch.uint16).to(dev),
+                     "codes": torch.from_numpy(m["codes"]).to(dev),
+                     "exp_bias": torch.from_numpy(m["exp_bias"]).to(dev)}
+    for s in range(warmup):
+        seedmm.moe(ids_d[s:s + 1], w_d[s:s + 1], x_d[s:s + 1], E, H, I, P, devm["gate"],
+                   devm["up"], devm["down"], y=y, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(warmup, warmup + steps):
+        seedmm.moe(ids_d[s:s + 1], w_d[s:s + 1], x_d[s:s + 1], E, H, I, P, devm["gate"],
+                   devm["up"], devm["down"], y=y, workspace=ws)
+    torch.cuda.synchronize()
+    out["resident_eager_ms_per_step"] = (time.perf_counter() - t0) / steps * 1e3
+    # host-to-device rate of one 256 MiB pinned copy
+    src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    out["pinned_h2d_GBps"] = 3 * (256 << 20) / (time.perf_counter() - t0) / 1e9
+    del cache, devm, src, dst
+    return out
 
 
 def encoder_bench(torch, seedmm, synth, P, no_cpu):
@@ -438,6 +513,9 @@ def main():
 
     if not args.no_mixed:
         out["mixed"] = mixed_bench(torch, seedmm, synth, dev, T, args.replicas, to_dev)
+
+    if not args.no_cache:
+        out["expert_cache"] = cache_bench(torch, seedmm, synth, host, P)
 
     if not args.no_encoder:
         out["encoder"] = encoder_bench(torch, seedmm, synth, P, args.no_cpu)

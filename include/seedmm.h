@@ -55,7 +55,9 @@ enum {
     SEEDMM_EINVAL = -1,     /* null pointer, bad size, bad P / dtype / exp_bias / ld   */
     SEEDMM_EALIGN = -2,     /* activation or output pointer / leading dim misaligned  */
     SEEDMM_EWORKSPACE = -3, /* workspace missing or smaller than seedmm_moe_workspace_bytes */
-    SEEDMM_EHIP = -4        /* the HIP runtime reported a launch failure              */
+    SEEDMM_EHIP = -4,       /* the HIP runtime reported a launch failure              */
+    SEEDMM_ECAPACITY = -5   /* an expert cache call routes to more distinct experts
+                               than the cache has slots                               */
 };
 
 enum { SEEDMM_F32 = 0, SEEDMM_BF16 = 1 };
@@ -204,6 +206,82 @@ int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int to
 int seedmm_search(const float *W, int ldw, const float *colw, int M, int K, int P,
                   int32_t exp_bias, uint16_t *seeds, uint16_t *coefs, uint8_t *codes,
                   double *err, void *hip_stream);
+
+/*
+ * Expert cache: routed experts resident in host memory, the recently used ones in device
+ * memory (NanoSeedLM README, "Highlights": the engine can keep the routed experts in
+ * RAM with a VRAM cache of the recently used ones, and "With the engine": a cache sized
+ * with --expert-cache-gb; documentation index, "Results": LRU beats LFU and a fixed hot
+ * set as the eviction policy).
+ *
+ * One cache serves one layer of E experts (gate/up [I][H], down [H][I], one P) with S
+ * device slots.  An expert is one RECORD of its nine streams, in the order gate.seeds,
+ * gate.coefs, gate.codes, up.seeds, ..., down.codes, each stream (the expert's own
+ * streams as in seedmm_moe: n*2, ceil(n*P/4)*2 and ceil(n/2) bytes, n = I*H/8) starting
+ * at a multiple of 256 bytes from the record start; seedmm_cache_record_layout gives the
+ * offsets and the record size (a multiple of 256).  Loading an expert copies its record.
+ * All memory is the caller's:
+ *   state      host memory of seedmm_cache_state_bytes(E, S) bytes, 8-byte aligned: the
+ *              bookkeeping (which expert sits in which slot, last use of each slot,
+ *              counters); it is the cache handle, used only by the calls below;
+ *   device     device memory of seedmm_cache_device_bytes(E, H, I, P, S) bytes,
+ *              256-byte aligned: S records and the device expert -> slot map;
+ *   host_pack  PINNED host memory (hipHostMalloc) of E records, expert e at byte
+ *              e * record; read by host-to-device copies only;
+ *   exp_bias   device int32[3][E]: the exp_bias of gate, up and down of every expert
+ *              (stays resident).
+ * Calls on one cache must not overlap (one host thread, one stream at a time); the
+ * host pack must stay unchanged while the cache is in use (seedmm_cache_reset after
+ * changing it).
+ */
+typedef struct seedmm_cache seedmm_cache;
+
+/* Record size in bytes, and the nine stream offsets into `offsets` (may be NULL); 0 for
+ * an invalid shape. */
+size_t seedmm_cache_record_layout(int H, int I, int P, size_t offsets[9]);
+size_t seedmm_cache_state_bytes(int E, int S);
+size_t seedmm_cache_device_bytes(int E, int H, int I, int P, int S);
+
+/* Initialise `state` as an empty cache.  Host only (no HIP call).  Requires E in
+ * [1, 4096], S in [1, E], P in {3, 4} and the layer shapes of seedmm_moe (H, I > 0,
+ * multiples of 8, with the stacking conditions on n = I*H/8: n*P % 4 == 0, n % 2 == 0).
+ * Errors: SEEDMM_EINVAL (null pointer, bad size, state_bytes or device_bytes too small),
+ * SEEDMM_EALIGN (state not 8-byte or device not 256-byte aligned). */
+int seedmm_cache_init(void *state, size_t state_bytes, int E, int H, int I, int P, int S,
+                      const void *host_pack, const int32_t *exp_bias, void *device,
+                      size_t device_bytes);
+
+/* Empty the cache and zero its counters (every expert is loaded again on its next use).
+ * Host only. */
+int seedmm_cache_reset(seedmm_cache *cache);
+
+/* The host half of one call, on its own: marks the distinct experts of topk_ids_host
+ * [T][top_k] used and assigns a slot to each that is not resident.  Resident experts are
+ * hits; each miss takes, in increasing expert order, the lowest free slot, else the slot
+ * whose expert was used longest ago (ties: lowest slot) among those this call does not
+ * use.  loads: host int32[2*S] receiving (expert, slot) pairs in that order (may be
+ * NULL); *n_loads their count.  Host only; the state changes only on success.
+ * Errors: SEEDMM_EINVAL (id outside [0, E), bad T / top_k), SEEDMM_ECAPACITY (more
+ * distinct experts than slots). */
+int seedmm_cache_plan(seedmm_cache *cache, const int32_t *topk_ids_host, int T, int top_k,
+                      int32_t *loads, int *n_loads);
+
+/* One routed layer call through the cache: seedmm_cache_plan on topk_ids_host, then on
+ * hip_stream one host-to-device copy of every loaded expert's record into its slot, the
+ * update of the device slot map, and the layer of seedmm_moe reading the experts from
+ * their slots.  topk_ids (device) must hold the same ids as topk_ids_host; the other
+ * arguments, results and errors are seedmm_moe's, plus SEEDMM_ECAPACITY; argument errors
+ * leave the state unchanged.  The output equals seedmm_moe's on the resident layer bit
+ * for bit.  If a copy or launch fails the cache is emptied and SEEDMM_EHIP returned. */
+int seedmm_cache_moe(seedmm_cache *cache, const int32_t *topk_ids_host,
+                     const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                     const void *x, float *y, void *workspace, size_t workspace_bytes,
+                     void *hip_stream);
+
+/* Counters since init or reset: out[0] calls, out[1] expert uses (distinct experts per
+ * call, summed), out[2] hits, out[3] misses (= records copied), out[4] bytes copied
+ * host-to-device. */
+int seedmm_cache_stats(const seedmm_cache *cache, uint64_t out[5]);
 
 /* Static description of a status code. */
 const char *seedmm_strerror(int status);

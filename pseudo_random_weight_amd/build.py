@@ -12,8 +12,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libseedmm.so")
-SOURCES = [os.path.join(CSRC, "seedmm.hip"), os.path.join(CSRC, "search.hip")]
-HEADERS = [os.path.join(CSRC, "seed_decode.hpp"), os.path.join(ROOT, "include", "seedmm.h")]
+SOURCES = [os.path.join(CSRC, "seedmm.hip"), os.path.join(CSRC, "search.hip"),
+           os.path.join(CSRC, "expert_cache.hip")]
+HEADERS = [os.path.join(CSRC, "seed_decode.hpp"), os.path.join(CSRC, "moe_layer.hpp"),
+           os.path.join(ROOT, "include", "seedmm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include "../../include/seedmm.h"
+#include "moe_layer.hpp"
 #include "seed_decode.hpp"
 
 namespace seedmm {
@@ -133,13 +134,24 @@ __device__ __forceinline__ int64_t coef_words_before(const uint32_t* p4mask, int
     return (nblk / 4) * (3 * (int64_t)e + n4);
 }
 
+// slot (device int32[E], or null): an expert cache, where expert e's streams sit in slot
+// slot[e] and slot s starts slot_stride bytes after slot s - 1 (m's pointers are slot 0's
+// streams); its exp_bias stays at index e.  Slots are used with one P only.
 __device__ __forceinline__ Mat mat_of(const seedmm_mat& m, int e, int64_t nblk, int P,
                                       int eb_scalar, bool eb_from_ptr,
-                                      const uint32_t* p4mask = nullptr) {
+                                      const uint32_t* p4mask = nullptr,
+                                      const int32_t* slot = nullptr, int64_t slot_stride = 0) {
     Mat r;
-    r.seeds = m.seeds + (int64_t)e * nblk;
-    r.coefs = m.coefs + coef_words_before(p4mask, e, nblk, P);
-    r.codes = m.codes + (int64_t)e * (nblk / 2);
+    if (slot) {
+        const int64_t off = (int64_t)slot[e] * slot_stride;
+        r.seeds = (const uint16_t*)((const char*)m.seeds + off);
+        r.coefs = (const uint16_t*)((const char*)m.coefs + off);
+        r.codes = m.codes + off;
+    } else {
+        r.seeds = m.seeds + (int64_t)e * nblk;
+        r.coefs = m.coefs + coef_words_before(p4mask, e, nblk, P);
+        r.codes = m.codes + (int64_t)e * (nblk / 2);
+    }
     r.exp_bias = eb_from_ptr ? m.exp_bias[e] : eb_scalar;
     return r;
 }
@@ -297,6 +309,9 @@ struct MfmaArgs {
     const int32_t* ids;     // one token (T = 1): topk_ids, workgroup y serves slot y
     const uint32_t* p4mask; // mixed packs: bit e set = expert e has P = 4; this launch
                             // serves the experts of its own P only (null: one P)
+    const int32_t* slot;    // expert cache: int32[E], slot of expert e's streams (null:
+                            // stacked experts, expert e at position e)
+    int64_t slot_stride;    // expert cache: bytes from one slot to the next
 };
 
 // Pair lists of the one-token path: slot y's list is the single pair index y.
@@ -450,8 +465,8 @@ __device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, cons
     L.q = lane >> 4;
     L.nbpr = a.K / 8;
     const int64_t nblk = (int64_t)a.M * L.nbpr;
-    if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask);
-    else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask);
+    if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask, a.slot, a.slot_stride);
+    else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
     const int m0 = blockIdx.x * 16 * RT;
     const int row = m0 + 16 * (wave / KS % RT) + r;
     L.rv = row < a.M;
@@ -614,9 +629,9 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     // ---- regeneration role: A row `arow` (matrix dmat, row drow), block lane dj ------
     const int arow = tid >> 2, dj = tid & 3;
     const int dmat = arow / RM, drow = arow % RM;
-    Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask);
+    Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
     if constexpr (NMAT == 2) {
-        if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask);
+        if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask, a.slot, a.slot_stride);
     }
     const bool drv = m0 + drow < M;
     const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
@@ -1016,6 +1031,7 @@ const char* seedmm_strerror(int status) {
         case SEEDMM_EALIGN: return "misaligned pointer or leading dimension";
         case SEEDMM_EWORKSPACE: return "workspace missing or too small";
         case SEEDMM_EHIP: return "HIP launch failure";
+        case SEEDMM_ECAPACITY: return "more distinct experts in one call than cache slots";
         default: return "unknown status";
     }
 }
@@ -1102,14 +1118,12 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I) {
 
 }  // extern "C"
 
-namespace {
+namespace seedmm_layer {
 
-// The routed layer; P = 3 or 4 for one P, or P = 0 with p4mask (device, bit e = expert e
-// has P = 4) for mixed packs, whose expert kernels run once per P.
 int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
             float* y, int E, int H, int I, int P, const uint32_t* p4mask, seedmm_mat gate,
             seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
-            void* hip_stream, void* const* events) {
+            void* hip_stream, void* const* events, const int32_t* slot, int64_t slot_stride) {
     if (T < 0 || E < 1 || E > 4096 || top_k < 1 || top_k > E || top_k > 64) return SEEDMM_EINVAL;
     if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0) return SEEDMM_EINVAL;
     if (P == 0 ? !p4mask : (P != 3 && P != 4)) return SEEDMM_EINVAL;
@@ -1158,6 +1172,8 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     a.h = hbuf; a.ldy = I;
     a.ids = one ? topk_ids : nullptr;
     a.p4mask = p4mask;
+    a.slot = slot;
+    a.slot_stride = slot_stride;
     mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
     mark(2);
 
@@ -1169,6 +1185,8 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     b.topk_w = topk_w; b.y = obuf; b.ldy = H;
     b.ids = a.ids;
     b.p4mask = p4mask;
+    b.slot = slot;
+    b.slot_stride = slot_stride;
     mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
     mark(3);
 
@@ -1179,7 +1197,9 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     return launch_status();
 }
 
-}  // namespace
+}  // namespace seedmm_layer
+
+using seedmm_layer::moe_run;
 
 extern "C" {
 
@@ -1189,7 +1209,7 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
                      void* hip_stream, void* const* events) {
     if (P != 3 && P != 4) return SEEDMM_EINVAL;
     return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, P, nullptr, gate, up, down,
-                   workspace, workspace_bytes, hip_stream, events);
+                   workspace, workspace_bytes, hip_stream, events, nullptr, 0);
 }
 
 int seedmm_moe_mixed(const int32_t* topk_ids, const float* topk_w, int T, int top_k,
@@ -1198,7 +1218,7 @@ int seedmm_moe_mixed(const int32_t* topk_ids, const float* topk_w, int T, int to
                      size_t workspace_bytes, void* hip_stream) {
     if (!p4mask) return SEEDMM_EINVAL;
     return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, 0, p4mask, gate, up, down,
-                   workspace, workspace_bytes, hip_stream, nullptr);
+                   workspace, workspace_bytes, hip_stream, nullptr, nullptr, 0);
 }
 
 int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libseedmm.so")
 
-OK, EINVAL, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EALIGN, EWORKSPACE, EHIP, ECAPACITY = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 
 
@@ -49,11 +49,25 @@ def _load():
     L.seedmm_search.argtypes = [p, i32, p, i32, i32, i32, ctypes.c_int32, p, p, p, p, p]
     L.seedmm_moe_mixed.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, p, SeedMat, SeedMat,
                                    SeedMat, p, ctypes.c_size_t, p]
+    sz = ctypes.c_size_t
+    L.seedmm_cache_state_bytes.restype = sz
+    L.seedmm_cache_state_bytes.argtypes = [i32, i32]
+    L.seedmm_cache_device_bytes.restype = sz
+    L.seedmm_cache_device_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.seedmm_cache_record_layout.restype = sz
+    L.seedmm_cache_record_layout.argtypes = [i32, i32, i32, p]
+    L.seedmm_cache_init.argtypes = [p, sz, i32, i32, i32, i32, i32, p, p, p, sz]
+    L.seedmm_cache_reset.argtypes = [p]
+    L.seedmm_cache_plan.argtypes = [p, p, i32, i32, p, p]
+    L.seedmm_cache_moe.argtypes = [p, p, p, p, i32, i32, p, p, p, sz, p]
+    L.seedmm_cache_stats.argtypes = [p, p]
     L.seedmm_strerror.restype = ctypes.c_char_p
     L.seedmm_strerror.argtypes = [i32]
     L.seedmm_version.restype = i32
     for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-                 "seedmm_moe", "seedmm_moe_timed", "seedmm_search", "seedmm_moe_mixed"):
+                 "seedmm_moe", "seedmm_moe_timed", "seedmm_search", "seedmm_moe_mixed",
+                 "seedmm_cache_init", "seedmm_cache_reset", "seedmm_cache_plan",
+                 "seedmm_cache_moe", "seedmm_cache_stats"):
         getattr(L, name).restype = i32
     return L
 
@@ -62,7 +76,10 @@ _lib = _load()
 
 EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
            "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_mixed",
-           "seedmm_search", "seedmm_strerror", "seedmm_version")
+           "seedmm_search", "seedmm_cache_record_layout", "seedmm_cache_state_bytes",
+           "seedmm_cache_device_bytes",
+           "seedmm_cache_init", "seedmm_cache_reset", "seedmm_cache_plan", "seedmm_cache_moe",
+           "seedmm_cache_stats", "seedmm_strerror", "seedmm_version")
 
 
 def lib():
@@ -257,3 +274,92 @@ def search(W: torch.Tensor, P: int, exp_bias: int, colw: torch.Tensor = None, er
     if err:
         out["err"] = e
     return out
+
+
+class ExpertCache:
+    """A layer whose routed experts live in pinned host memory, with S device slots for
+    the recently used ones (seedmm_cache_*).  host: {"gate", "up", "down"} -> dicts of
+    numpy streams (seeds, coefs, codes, exp_bias) stacked as for moe(); they are packed
+    once into expert records in pinned host memory (offsets from
+    seedmm_cache_record_layout), and the exp_bias arrays go to device memory."""
+
+    def __init__(self, host: dict, E: int, H: int, I: int, P: int, S: int, device="cuda"):
+        import numpy as np
+        self.E, self.H, self.I, self.P, self.S = E, H, I, P, S
+        offs = (ctypes.c_size_t * 9)()
+        rec = int(_lib.seedmm_cache_record_layout(H, I, P, offs))
+        nstate = int(_lib.seedmm_cache_state_bytes(E, S))
+        ndev = int(_lib.seedmm_cache_device_bytes(E, H, I, P, S))
+        if rec == 0 or nstate == 0 or ndev == 0:
+            raise SeedmmError(EINVAL, "seedmm_cache sizes")
+        self.record_bytes = rec
+        pack = torch.zeros(E * rec, dtype=torch.uint8, pin_memory=True)
+        view = pack.numpy().reshape(E, rec)
+        for m, n in enumerate(("gate", "up", "down")):
+            for k, part in enumerate(("seeds", "coefs", "codes")):
+                a = np.ascontiguousarray(host[n][part]).view(np.uint8).reshape(E, -1)
+                o = offs[3 * m + k]
+                view[:, o:o + a.shape[1]] = a
+        self._pack = pack
+        eb = np.stack([np.asarray(host[n]["exp_bias"], dtype=np.int32) for n in ("gate", "up", "down")])
+        self._exp_bias = torch.from_numpy(np.ascontiguousarray(eb)).to(device)
+        self._state = torch.empty((nstate + 7) // 8, dtype=torch.int64)   # host, 8-byte aligned
+        self._device = torch.empty(ndev + 256, dtype=torch.uint8, device=device)
+        off = (-self._device.data_ptr()) % 256
+        _check(_lib.seedmm_cache_init(self.handle, nstate, E, H, I, P, S,
+                                      ctypes.c_void_p(pack.data_ptr()),
+                                      ctypes.c_void_p(self._exp_bias.data_ptr()),
+                                      ctypes.c_void_p(self._device.data_ptr() + off), ndev),
+               "seedmm_cache_init")
+
+    @property
+    def handle(self):
+        return ctypes.c_void_p(self._state.data_ptr())
+
+    @property
+    def device_bytes(self) -> int:
+        return int(_lib.seedmm_cache_device_bytes(self.E, self.H, self.I, self.P, self.S))
+
+    def reset(self):
+        _check(_lib.seedmm_cache_reset(self.handle), "seedmm_cache_reset")
+
+    def plan(self, topk_ids_host):
+        """Host-only plan of one call: [(expert, slot), ...] loads (changes the state)."""
+        import numpy as np
+        ids = np.ascontiguousarray(topk_ids_host, dtype=np.int32)
+        T, k = ids.shape
+        loads = np.zeros(2 * self.S, dtype=np.int32)
+        n = ctypes.c_int(0)
+        _check(_lib.seedmm_cache_plan(self.handle, ids.ctypes.data_as(ctypes.c_void_p), T, k,
+                                      loads.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)),
+               "seedmm_cache_plan")
+        return [(int(loads[2 * i]), int(loads[2 * i + 1])) for i in range(n.value)]
+
+    def moe(self, topk_ids_host, topk_ids, topk_w, x, y=None, workspace=None, stream=None):
+        """The routed layer through the cache (seedmm_cache_moe); topk_ids_host is the
+        host copy (numpy int32 [T][top_k]) of the device topk_ids."""
+        import numpy as np
+        ids_h = np.ascontiguousarray(topk_ids_host, dtype=np.int32)
+        _dev(topk_ids, torch.int32, "topk_ids")
+        _dev(topk_w, torch.float32, "topk_w")
+        _dev(x, torch.bfloat16, "x")
+        T, k = topk_ids.shape
+        if ids_h.shape != (T, k):
+            raise ValueError("topk_ids_host and topk_ids differ in shape")
+        if y is None:
+            y = torch.empty((T, self.H), dtype=torch.float32, device=x.device)
+        _dev(y, torch.float32, "y")
+        if workspace is None:
+            workspace = torch.empty(moe_workspace_bytes(T, k, self.E, self.H, self.I),
+                                    dtype=torch.uint8, device=x.device)
+        _check(_lib.seedmm_cache_moe(self.handle, ids_h.ctypes.data_as(ctypes.c_void_p),
+                                     _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y),
+                                     _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream)), "seedmm_cache_moe")
+        return y
+
+    def stats(self) -> dict:
+        out = (ctypes.c_uint64 * 5)()
+        _check(_lib.seedmm_cache_stats(self.handle, out), "seedmm_cache_stats")
+        return dict(zip(("calls", "uses", "hits", "misses", "bytes"), (int(v) for v in out)))
