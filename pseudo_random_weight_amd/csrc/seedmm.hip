@@ -79,6 +79,17 @@ struct Seg {
             }
         }
     }
+    // VEC: the loaded words are needed here (an empty asm reads them), so the loads
+    // complete before this point and cannot be moved past it into a later iteration
+    __device__ __forceinline__ void hold() const {
+        static_assert(VEC, "vector-load segments only");
+        if constexpr (P == 4)
+            asm volatile("" ::"v"(sd[0]), "v"(sd[1]), "v"(sd[2]), "v"(sd[3]), "v"(cf[0]),
+                         "v"(cf[1]), "v"(cf[2]), "v"(cf[3]), "v"(cd));
+        else
+            asm volatile("" ::"v"(sd[0]), "v"(sd[1]), "v"(sd[2]), "v"(sd[3]), "v"(cf[0]),
+                         "v"(cf[1]), "v"(cf[2]), "v"(cd));
+    }
     __device__ __forceinline__ uint32_t seed(int s) const {
         if constexpr (VEC) return __builtin_amdgcn_ubfe(sd[s >> 1], 16 * (s & 1), 16);
         else return s1[s];
@@ -338,10 +349,12 @@ __device__ __forceinline__ Window window_of(uint32_t seed16, const uint32_t* tab
 // One pass over this wave's share of K for NTA token tiles.  Branch-free: addresses are
 // clamped into range and padding blocks get all-zero coefficients, which decode to exact
 // zero weights.  The stream words of the next segment are loaded while the current one
-// is regenerated.
-template <int P, bool VEC, int NTA, int KS, bool TAB>
+// is regenerated.  XL: the single token's activation row sits in LDS (xs, K bf16), so
+// the stream words are the loop's only global loads.
+template <int P, bool VEC, int NTA, int KS, bool TAB, bool XL = false>
 __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const* brow,
-                                            f32x4* acc) {
+                                            f32x4* acc, const uint16_t* xs = nullptr) {
+    static_assert(!XL || NTA == 1, "the LDS activation row serves one token");
     constexpr int GSTRIDE = KS * 4;
     auto seg = [&](int it, int& gc, int& nvalid) {
         const int g = it * GSTRIDE + L.ks * 4 + L.q;
@@ -357,6 +370,8 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
         seg(it + 1 < L.n_it ? it + 1 : it, gn, nvn);
         Seg<P, VEC> nxt;
         nxt.load(L.W.seeds, L.W.coefs, L.W.codes, L.rowb + gn * 8, VEC ? 8 : nvn);
+        // one-token kernel: issue those loads here, ahead of this segment's work
+        if constexpr (XL && VEC) __builtin_amdgcn_sched_barrier(0);
         cur.clear_coefs_unless(nvalid > 0);   // VEC segments are whole or absent
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -369,9 +384,16 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
             const int kb = VEC ? gc * 8 + s : min(gc * 8 + s, L.nbpr - 1);
 #pragma unroll
             for (int t = 0; t < NTA; ++t) {
-                const bf16x8 B = load_bf16x8(brow[t] + 8 * kb);
+                const bf16x8 B = XL ? *(const bf16x8*)(xs + 8 * kb)
+                                    : load_bf16x8(brow[t] + 8 * kb);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
             }
+        }
+        // one-token kernel: the next segment's words arrive during this iteration (the
+        // barrier keeps their wait after this segment's work)
+        if constexpr (XL && VEC) {
+            __builtin_amdgcn_sched_barrier(0);
+            nxt.hold();
         }
         cur = nxt;
         gc = gn;
@@ -380,10 +402,10 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
 }
 
 // One pass: NTA tiles of 16 tokens starting at token slot `pass`.
-template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB, int RT>
+template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB, int RT, bool XL = false>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, const int32_t* list,
                                           int n_e, int pass, int m0, int wave, int lane, int r,
-                                          f32x4 (*red)[NT][64]) {
+                                          f32x4 (*red)[NT][64], const uint16_t* xs = nullptr) {
     constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;   // waves sharing one K range
     // B rows of this lane (token column r of every tile); slots past n_e repeat the last
     // token so every load stays in range -- their outputs are never stored.
@@ -400,7 +422,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
     f32x4 acc[NTA];
 #pragma unroll
     for (int t = 0; t < NTA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_k_loop<P, VEC, NTA, KS, TAB>(L, brow, acc);
+    mfma_k_loop<P, VEC, NTA, KS, TAB, XL>(L, brow, acc, xs);
 
     // partial sums of the four waves meet in LDS (fixed order); wave c % 4 finishes the
     // (row tile, token tile) pair c
@@ -453,11 +475,13 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
 // 4 waves on 16 weight rows.  GATEUP: waves 0-1 regenerate gate, waves 2-3 up, each
 // over half of K; otherwise the 4 waves take a quarter of K each.
 // The products of one workgroup once its expert (e, n_e pairs in `list`) is known.
-template <int P, bool VEC, int NT, int MODE, bool TAB, int RT>
+template <int P, bool VEC, int NT, int MODE, bool TAB, int RT, bool XL = false>
 __device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, const int32_t* list,
-                                         const uint32_t* tab, f32x4 (*red)[NT][64]) {
+                                         const uint32_t* tab, f32x4 (*red)[NT][64],
+                                         const uint16_t* xs = nullptr) {
     constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15;
     Lane L;
     L.tab = TAB ? tab : nullptr;
@@ -465,8 +489,14 @@ __device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, cons
     L.q = lane >> 4;
     L.nbpr = a.K / 8;
     const int64_t nblk = (int64_t)a.M * L.nbpr;
-    if (MODE == MODE_GATEUP && wave >= KS) L.W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask, a.slot, a.slot_stride);
-    else L.W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
+    // gate/up: waves KS.. regenerate up (field-wise selects keep the pointers scalar)
+    const bool second = MODE == MODE_GATEUP && wave >= KS;
+    seedmm_mat src;
+    src.seeds = second ? a.A2.seeds : a.A.seeds;
+    src.coefs = second ? a.A2.coefs : a.A.coefs;
+    src.codes = second ? a.A2.codes : a.A.codes;
+    src.exp_bias = second ? a.A2.exp_bias : a.A.exp_bias;
+    L.W = mat_of(src, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
     const int m0 = blockIdx.x * 16 * RT;
     const int row = m0 + 16 * (wave / KS % RT) + r;
     L.rv = row < a.M;
@@ -474,14 +504,18 @@ __device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, cons
     L.nseg = (L.nbpr + 7) / 8;
     L.n_it = (L.nseg + KS * 4 - 1) / (KS * 4);
 
-    for (int pass = 0; pass < n_e; pass += NT * 16) {
-        const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
-        static_assert(NT == 4, "the decode kernel holds at most 4 token tiles");
-        switch (ntiles) {
-            case 1: mfma_pass<P, VEC, 1, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
-            case 2: mfma_pass<P, VEC, 2, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
-            case 3: mfma_pass<P, VEC, 3, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
-            default: mfma_pass<P, VEC, 4, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+    if constexpr (NT == 1) {   // one token (n_e == 1)
+        mfma_pass<P, VEC, 1, MODE, NT, TAB, RT, XL>(a, L, list, n_e, 0, m0, wave, lane, r, red, xs);
+    } else {
+        static_assert(NT == 4, "the decode kernel holds 1 or at most 4 token tiles");
+        for (int pass = 0; pass < n_e; pass += NT * 16) {
+            const int ntiles = min(NT, (n_e - pass + 15) / 16);   // uniform
+            switch (ntiles) {
+                case 1: mfma_pass<P, VEC, 1, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+                case 2: mfma_pass<P, VEC, 2, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+                case 3: mfma_pass<P, VEC, 3, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+                default: mfma_pass<P, VEC, 4, MODE, NT, TAB, RT>(a, L, list, n_e, pass, m0, wave, lane, r, red); break;
+            }
         }
     }
 }
@@ -533,6 +567,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 2
     if (n_e <= 0) return;
     if constexpr (TAB) fill_lfsr_tables(tab);
     mfma_run<P, VEC, NT, MODE, TAB, RT>(a, e, n_e, list, tab, red);
+}
+
+// One token (T = 1): workgroup row y serves slot y of the token.  The same products as
+// k_mfma's one-token path (bit for bit), with the activation row (x for gate/up, the
+// slot's h row for down) staged once in LDS and a register budget of 2 waves per SIMD
+// (one wave round fills the chip at T = 1), so each segment's stream loads can be in
+// flight while the previous segment is regenerated.  Dynamic LDS: K bf16.
+template <int P, bool VEC, int MODE, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mfma_one(const MfmaArgs a) {
+    static_assert(MODE != MODE_GEMM, "one-token kernel of the routed layer");
+    __shared__ f32x4 red[4][1][64];
+    __shared__ uint32_t tab[512];
+    extern __shared__ uint4 xs[];
+    const int e = a.ids[blockIdx.y];
+    if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
+    if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
+    const int64_t row = MODE == MODE_GATEUP ? 0 : (int64_t)blockIdx.y;
+    const uint4* src = (const uint4*)(a.x + row * a.ldx);
+    for (int i = threadIdx.x; i < a.K / 8; i += 256) xs[i] = src[i];
+    fill_lfsr_tables(tab);   // its barrier also publishes xs
+    mfma_run<P, VEC, 1, MODE, true, RT, true>(a, e, 1, kSlotIota + blockIdx.y, tab, red,
+                                              (const uint16_t*)xs);
 }
 
 // ----------------------------------------------------------------------------------
@@ -973,6 +1029,8 @@ void gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int eb, co
 
 // Decode shape: 4 waves split K, up to 64 tokens per pass.  Prefill shape: 4 waves on
 // 4 row tiles, up to 256 tokens per pass.
+constexpr int kOneMaxK = 16384;   // one-token kernel: activation row of at most 32 KB in LDS
+
 template <int P, bool VEC, int MODE>
 void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     if (prefill && VEC && a.K % 256 == 0) {
@@ -983,6 +1041,13 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
         // down and the plain product: two 16-row tiles per workgroup, K in halves
         constexpr int RT = MODE == MODE_GATEUP ? 1 : 2;
         dim3 grid((a.M + 16 * RT - 1) / (16 * RT), gridy);
+        if constexpr (MODE != MODE_GEMM) {
+            if (a.ids && a.K <= kOneMaxK) {
+                hipLaunchKernelGGL((k_mfma_one<P, VEC, MODE, RT>), grid, dim3(256),
+                                   (size_t)a.K * 2, st, a);
+                return;
+            }
+        }
         hipLaunchKernelGGL((k_mfma<P, VEC, 4, MODE, true, RT>), grid, dim3(256), 0, st, a);
     }
 }
