@@ -270,6 +270,25 @@ def test_moe_output_independent_of_batch(sm):
         assert np.array_equal(y_one.view(np.uint32), y_big[t:t + 1].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("E,H,I,P,k", [
+    (6, 200, 136, 4, 2),      # K % 64 != 0: the per-block stream path
+    (12, 2048, 1024, 3, 4),   # P = 3, vector path
+    (4, 16640, 64, 4, 2),     # gate/up K above the one-token kernel's LDS row limit
+])
+def test_one_token_matches_its_batch_and_the_oracle(sm, oracle, E, H, I, P, k):
+    """One token runs the one-token kernels (activation row in LDS) unless K is too long
+    for them; either way its output equals the same token's inside a 3-token batch bit
+    for bit, and the oracle within tolerance."""
+    say("one token", E, H, I, P, k)
+    gate, up, down, ids, w, x = moe_case(3, E, H, I, P, k, 4, f"one{H}x{I}")
+    y3, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    for t in range(3):
+        y1, _ = run_moe(sm, gate, up, down, ids[t:t + 1], w[t:t + 1], x[t:t + 1], E, H, I, P)
+        assert np.array_equal(y1.view(np.uint32), y3[t:t + 1].view(np.uint32)), t
+        ref = oracle.moe(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, P, gate, up, down)
+        assert rel_l2(y1[0], ref[0]) <= 1e-2, t
+
+
 def test_moe_graph_replays_match_eager(sm):
     """The layer call captured in a HIP graph: every replay, with eager work and
     synchronisations between replays, gives the eager result bit for bit."""
