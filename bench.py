@@ -442,8 +442,9 @@ def main():
         return wall / steps, distinct, np.percentile(per, [10, 50, 90])
 
     # stage times and the roofline come from eager launches with HIP events around each
-    # kernel; the step time is HIP-graph replays unless --eager
-    t_eager, stages, distinct, ids_h, x_d, w_d = run(T, args.warmup, args.steps)
+    # kernel; the step time is HIP-graph replays unless --eager.  The eager run gets 30
+    # more warm-up steps: the first ~12 launches after start run ~10% slower (clock ramp)
+    t_eager, stages, distinct, ids_h, x_d, w_d = run(T, args.warmup + 30, args.steps)
     pct = None
     if args.eager:
         t_step = t_eager
