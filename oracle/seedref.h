@@ -13,7 +13,7 @@
  *       w_i = 2^(code + exp_bias - 15) * sum_j c_j * (s_{iP+j+1} - 32768),  i = 0..7
  *   where s_1, s_2, ... are the successive states of the register started at the seed.
  *
- * Readings of points the pages leave open (all are listed in the design doc):
+ * Readings of points the pages leave open:
  *   - register: 16-bit Fibonacci, shifts left, new bit = parity(state & 0xB400)
  *     enters bit 0 (polynomial x^16 + x^14 + x^13 + x^11 + 1, period 65,535);
  *   - basis: states after steps 1..8P fill the 8 x P basis row-major;

@@ -6,7 +6,7 @@ rounding of the drawn activations) and lays them out in the stream sizes of the
 tensor encoding (NAME.seeds U16, NAME.coefs U16, NAME.codes U8, NAME.exp_bias I32,
 model card "K2-Horizon-MoVA-36B-A4B - NanoSeedLM p4mx-q4v", section "This upload").
 
-Recipe (also stated in the design doc):
+Recipe:
   * seeds uniform in [1, 65535];
   * coefficient nibbles uniform in [-8, 7] and exponent codes uniform in [0, 15];
     both are uniform 4-bit fields, so their packed streams are uniform random words
