@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/seedmm.h"
 #include "seed_decode.hpp"
 
@@ -92,6 +94,8 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
                                                 double* __restrict__ errs) {
 #pragma clang fp contract(off)
     __shared__ uint32_t res[4][2];   // per block: seed | code << 16, coefficient nibbles
+    __shared__ int qseed[4][128];    // per wave: queued seeds and their solutions
+    __shared__ double qalpha[4][128][P];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t b = (int64_t)blockIdx.x * 4 + wave;
     if (b < nblk) {
@@ -114,87 +118,179 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
         double best = __builtin_inf();
         int bkey = 0x7FFFFFFF;            // seed * 16 + code
         uint32_t bnib = 0;
-        for (int k = 0; k < 1024; ++k) {
-            const int seed = 1 + lane + 64 * k;
-            if (seed > 65535) break;
+
+        // Every code of one seed, from its solution alpha (the definition's arithmetic).
+        // Lanes see seeds in no particular order, so candidates compare on the whole key
+        // (err, seed * 16 + code).
+        auto try_codes = [&](int seed, const double (&alpha)[4]) {
             const Window win = lfsr_window((uint32_t)seed);
             int Ui[8][P];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < P; ++j) Ui[i][j] = (int)state(win, i * P + j + 1) - 32768;
+            // A NaN coefficient comes only from a NaN alpha (alpha * 2^-e is otherwise a
+            // number, and rint and the clamps keep it one), so the path is chosen once.
+            bool anynan = false;
+#pragma unroll
+            for (int j = 0; j < P; ++j) anynan |= alpha[j] != alpha[j];
+            auto codes_loop = [&](auto nanpath) {
+                constexpr bool NANP = decltype(nanpath)::value;
+#pragma unroll 1
+                for (int code = 0; code < 16; ++code) {
+                    const int e = code + exp_bias - 15;
+                    const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
+                    const int key = seed * 16 + code;
+                    int c[P];
+                    bool zero = true;
+#pragma unroll
+                    for (int j = 0; j < P; ++j) {
+                        double q = __builtin_rint(alpha[j] * inv);   // half to even
+                        if (q < -8.0) q = -8.0;
+                        if (q > 7.0) q = 7.0;
+                        c[j] = q != q ? (int)0x80000000 : (int)q;
+                        zero &= c[j] == 0;
+                    }
+                    if (zero) {
+                        // |alpha_j| / 2^e only shrinks as the code grows, so every larger
+                        // code rounds to zero as well, with error e0 and a larger key
+                        if (e0 < best || (e0 == best && key < bkey)) {
+                            best = e0;
+                            bkey = key;
+                            bnib = 0;
+                        }
+                        break;
+                    }
+                    double err = 0.0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        double v;
+                        if constexpr (!NANP) {
+                            int vi = 0;
+#pragma unroll
+                            for (int j = 0; j < P; ++j) vi += Ui[i][j] * c[j];
+                            v = (double)vi;
+                        } else {
+                            v = 0.0;
+#pragma unroll
+                            for (int j = 0; j < P; ++j) v += (double)Ui[i][j] * (double)c[j];
+                        }
+                        const double dd = w[i] - sc * v;
+                        err += WEIGHTED ? d[i] * (dd * dd) : dd * dd;
+                    }
+                    if (err < best || (err == best && key < bkey)) {
+                        best = err;
+                        bkey = key;
+                        uint32_t nib = 0;
+#pragma unroll
+                        for (int j = 0; j < P; ++j) nib |= ((uint32_t)c[j] & 0xFu) << (4 * j);
+                        bnib = nib;
+                    }
+                }
+            };
+            if (anynan) codes_loop(std::true_type{});
+            else codes_loop(std::false_type{});
+        };
+
+        // Seeds whose systems survive the bound below queue up in LDS; each time 64 are
+        // queued, every lane runs the code loop of one of them.
+        int qn = 0;                       // queued entries (wave-uniform)
+        double thr = __builtin_inf();     // best error found so far by this wave
+        auto run_batch = [&](int base, int n) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            if (lane < n) {
+                double al[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int j = 0; j < P; ++j) al[j] = qalpha[wave][base + lane][j];
+                try_codes(qseed[wave][base + lane], al);
+            }
+            double m = best;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m = fmin(m, __shfl_xor(m, off));
+            thr = m;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        };
+
+        for (int k = 0; k < 1024; ++k) {
+            const int seed = 1 + lane + 64 * k;
+            const bool valid = seed <= 65535;
+            const Window win = lfsr_window((uint32_t)(valid ? seed : 1));
             double U[8][P];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    Ui[i][j] = (int)state(win, i * P + j + 1) - 32768;
-                    U[i][j] = (double)Ui[i][j];
-                }
-            double a[4][4], r[4], alpha[4];
+                for (int j = 0; j < P; ++j) U[i][j] = (double)((int)state(win, i * P + j + 1) - 32768);
+            double a[4][4], r[4], r0[4], alpha[4];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 r[j] = 0.0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) r[j] += (WEIGHTED ? d[i] * U[i][j] : U[i][j]) * w[i];
+                r0[j] = r[j];
+                if constexpr (WEIGHTED) {
 #pragma unroll
-                for (int kk = 0; kk < P; ++kk) {
-                    a[j][kk] = 0.0;
+                    for (int kk = 0; kk < P; ++kk) {
+                        a[j][kk] = 0.0;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        a[j][kk] += (WEIGHTED ? d[i] * U[i][j] : U[i][j]) * U[i][kk];
+                        for (int i = 0; i < 8; ++i) a[j][kk] += (d[i] * U[i][j]) * U[i][kk];
+                    }
+                } else {
+                    // products of 16-bit integers and their partial sums (below 2^34) are
+                    // exact in double, so A_jk and A_kj are the same double
+#pragma unroll
+                    for (int kk = j; kk < P; ++kk) {
+                        a[j][kk] = 0.0;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) a[j][kk] += U[i][j] * U[i][kk];
+                    }
                 }
             }
-            if (!solve_small<P>(a, r, alpha)) continue;
-#pragma unroll 1
-            for (int code = 0; code < 16; ++code) {
-                const int e = code + exp_bias - 15;
-                const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
-                int c[P];
-                bool nan = false, zero = true;
+            if constexpr (!WEIGHTED) {
+#pragma unroll
+                for (int j = 0; j < P; ++j)
+#pragma unroll
+                    for (int kk = 0; kk < j; ++kk) a[j][kk] = a[kk][j];
+            }
+            double trace = 0.0;
+#pragma unroll
+            for (int j = 0; j < P; ++j) trace += a[j][j];
+            const bool ok = valid && solve_small<P>(a, r, alpha);
+
+            // Bound: every code's error is at least the least-squares residual
+            // R = e0 - r . alpha.  Elimination with partial pivoting on this system
+            // misses R by at most ~4 n eps kappa(A) e0, and kappa(A) <= trace^P / |det|
+            // (det = product of the pivots).  With that bound at most 1e7 the margin
+            // 1e-6 e0 covers it many times over, so a seed with
+            // (R - 1e-6 e0)(1 - 1e-12) > thr cannot reach an error <= thr, which some
+            // candidate already has: it cannot win, and skipping it changes nothing.
+            bool keep = ok;
+            if (ok && e0 > 0.0 && thr < __builtin_inf()) {
+                double det = 1.0, ra = 0.0, tp = 1.0;
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    double q = __builtin_rint(alpha[j] * inv);   // half to even
-                    if (q < -8.0) q = -8.0;
-                    if (q > 7.0) q = 7.0;
-                    nan |= q != q;
-                    c[j] = q != q ? (int)0x80000000 : (int)q;
-                    zero &= c[j] == 0;
+                    det *= a[j][j];
+                    ra += r0[j] * alpha[j];
+                    tp *= trace;
                 }
-                if (zero) {
-                    // |alpha_j| / 2^e only shrinks as the code grows, so every larger code
-                    // rounds to zero as well; they all have error e0 and, compared
-                    // strictly, none of them can replace this one
-                    if (e0 < best) {
-                        best = e0;
-                        bkey = seed * 16 + code;
-                        bnib = 0;
-                    }
-                    break;
-                }
-                double err = 0.0;
+                const double lb = ((e0 - ra) - 1e-6 * e0) * (1.0 - 1e-12);
+                if (tp <= 1e7 * fabs(det) && lb > thr) keep = false;
+            }
+            const uint64_t bal = __ballot(keep);
+            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+            if (keep) {
+                const int pos = qn + __popcll(below);
+                qseed[wave][pos] = seed;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    double v;
-                    if (!nan) {
-                        int vi = 0;
-#pragma unroll
-                        for (int j = 0; j < P; ++j) vi += Ui[i][j] * c[j];
-                        v = (double)vi;
-                    } else {
-                        v = 0.0;
-#pragma unroll
-                        for (int j = 0; j < P; ++j) v += U[i][j] * (double)c[j];
-                    }
-                    const double dd = w[i] - sc * v;
-                    err += WEIGHTED ? d[i] * (dd * dd) : dd * dd;
-                }
-                if (err < best) {
-                    best = err;
-                    bkey = seed * 16 + code;
-                    uint32_t nib = 0;
-#pragma unroll
-                    for (int j = 0; j < P; ++j) nib |= ((uint32_t)c[j] & 0xFu) << (4 * j);
-                    bnib = nib;
-                }
+                for (int j = 0; j < P; ++j) qalpha[wave][pos][j] = alpha[j];
+            }
+            qn += __popcll(bal);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            if (qn >= 64) {
+                run_batch(qn - 64, 64);
+                qn -= 64;
             }
         }
+        if (qn > 0) run_batch(0, qn);
         // lexicographic minimum of (err, seed, code) over the wave
         const int own = bkey;
         double gb = best;
