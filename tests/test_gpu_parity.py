@@ -422,6 +422,64 @@ def test_search_matches_oracle_bit_for_bit(sm, oracle, P, weighted):
     np.testing.assert_array_equal(got["err"].cpu().numpy().view(np.uint64), ref["err"].view(np.uint64))
 
 
+@pytest.mark.parametrize("P,weighted", [(4, False), (3, False), (4, True)])
+def test_search_edge_blocks_match_oracle(sm, oracle, P, weighted):
+    """Blocks at the edges of the seed bound, against the oracle bit for bit: all zero
+    (nothing to bound), constant, too small for any nonzero coefficient, large enough
+    to clamp, exact seed-coded blocks (best error 0), a single nonzero weight, and with
+    importance weights, columns of weight 0."""
+    import torch
+    say("search edge blocks", P, weighted)
+    base = synth.config_seed(9)
+    planted = oracle.reconstruct_f32(synth.seed_matrix(base, f"edge{P}", 1, 16, P), 1, 16, P)[0]
+    rnd = synth.normal_f32(base, "edge.r", (8,))
+    blocks = [
+        np.zeros(8, np.float32),
+        np.full(8, 0.01, np.float32),
+        np.full(8, -3.0e-3, np.float32),
+        (rnd * 1e-12).astype(np.float32),
+        (rnd * 50.0).astype(np.float32),
+        planted[:8], planted[8:],
+        np.array([0, 0, 0, 0.02, 0, 0, 0, 0], np.float32),
+        (rnd * 0.02).astype(np.float32),
+    ]
+    W = np.concatenate(blocks)[None, :]                 # one row of 9 blocks (ragged group)
+    K = W.shape[1]
+    colw = None
+    if weighted:
+        colw = np.abs(synth.normal_f32(base, "edge.cw", (K,))).astype(np.float32) + 0.1
+        colw[::3] = 0.0                                  # some columns carry no weight
+    ref = oracle.search_matrix(W, P, -4, colw)
+    got = sm.search(torch.from_numpy(W).cuda(), P, -4,
+                    None if colw is None else torch.from_numpy(colw).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got["seeds"].cpu().view(torch.int16).numpy().view(np.uint16), ref["seeds"])
+    np.testing.assert_array_equal(got["coefs"].cpu().view(torch.int16).numpy().view(np.uint16), ref["coefs"])
+    np.testing.assert_array_equal(got["codes"].cpu().numpy(), ref["codes"])
+    np.testing.assert_array_equal(got["err"].cpu().numpy().view(np.uint64), ref["err"].view(np.uint64))
+
+
+@pytest.mark.parametrize("P,weighted,M", [(4, False, 4), (3, True, 2)])
+def test_search_many_blocks_match_oracle(sm, oracle, P, weighted, M):
+    """Many random blocks (256 or 128), so the seed bound prunes in every state of the
+    running best: the whole encoding equals the oracle's bit for bit."""
+    import torch
+    K = 512
+    say("search many blocks", P, weighted, M * K // 8)
+    W = _search_case(M, K, f"many{P}{weighted}")
+    colw = None
+    if weighted:
+        colw = np.abs(synth.normal_f32(synth.config_seed(7), f"cwm{P}", (K,))).astype(np.float32) + 0.1
+    ref = oracle.search_matrix(W, P, -4, colw)
+    got = sm.search(torch.from_numpy(W).cuda(), P, -4,
+                    None if colw is None else torch.from_numpy(colw).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got["seeds"].cpu().view(torch.int16).numpy().view(np.uint16), ref["seeds"])
+    np.testing.assert_array_equal(got["coefs"].cpu().view(torch.int16).numpy().view(np.uint16), ref["coefs"])
+    np.testing.assert_array_equal(got["codes"].cpu().numpy(), ref["codes"])
+    np.testing.assert_array_equal(got["err"].cpu().numpy().view(np.uint64), ref["err"].view(np.uint64))
+
+
 @pytest.mark.parametrize("P", [4, 3])
 def test_search_recovers_a_seed_coded_matrix(sm, oracle, P):
     """A matrix decoded from random streams is an exact fit: the GPU encoding decodes back
