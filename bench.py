@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "effective weights/s + compressed HBM GB/s (% roofline); MoE-layer decode tok/s"
 HBM_PEAK = 8.0e12                 # bytes/s, MI355X HBM3E
 VALU_PEAK = 256 * 4 * 16 * 2.4e9  # lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+MFMA_PEAK = 2.5e15                 # flop/s, dense bf16 matrix cores
 E, H, I, TOPK = 100, 2048, 1024, 8
 
 
@@ -55,6 +56,8 @@ def parse():
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--no-encoder", action="store_true",
                     help="skip the seed-search (encoder) measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (single GEMV, one expert, P = 3, prefill)")
     ap.add_argument("--no-cache", action="store_true",
                     help="skip the host-resident experts with a device expert cache")
     ap.add_argument("--no-mixed", action="store_true",
@@ -151,6 +154,131 @@ def warm_replays(torch, graphs, seconds=0.03):
     for s_ in range(int(seconds / est)):
         graphs[s_ % len(graphs)].replay()
     torch.cuda.synchronize()
+
+
+def graph_step(torch, calls, steps):
+    """Wall time per step of HIP-graph replays of `calls` (one captured graph per input
+    set, cycled), after an untimed warm-up."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for c in calls:
+        G = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(G):
+            c()
+        graphs.append(G)
+    warm_replays(torch, graphs)
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        graphs[s_ % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    del graphs
+    return t
+
+
+def config_lines(torch, seedmm, synth, reps, to_dev):
+    """One timed figure for each of the other workloads: the single matrix-vector product
+    (256 x 512, fp32 x), one SwiGLU expert (2048 -> 768 -> 2048) at 1 and 8 tokens, the
+    P = 3 layer at 1 and 16 tokens, and 4096-token prefill through the P = 4 layer."""
+    dev = torch.device("cuda:0")
+    out = {}
+    # C1: back-to-back launches on the default stream (launch overhead included), on one
+    # matrix (warm caches) and rotating over 8192 copies (604 MB, beyond the 256 MB cache)
+    M1, K1, R1 = 256, 512, 8192
+    base = synth.config_seed(0)
+    m = synth.seed_matrix(base, "bench.C1", M1, K1, 4)
+    seeds = torch.from_numpy(np.tile(m["seeds"].view(np.int16), R1).reshape(R1, -1)).view(torch.uint16).to(dev)
+    coefs = torch.from_numpy(np.tile(m["coefs"].view(np.int16), R1).reshape(R1, -1)).view(torch.uint16).to(dev)
+    codes = torch.from_numpy(np.tile(m["codes"], R1).reshape(R1, -1)).to(dev)
+    mats = [{"seeds": seeds[r], "coefs": coefs[r], "codes": codes[r], "exp_bias_host": m["exp_bias"]}
+            for r in range(R1)]
+    x = torch.from_numpy(synth.normal_f32(base, "bench.C1.x", (K1,))).to(dev)
+    y = torch.empty(M1, dtype=torch.float32, device=dev)
+
+    def launches(n, rot):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            seedmm.gemv(mats[i % R1 if rot else 0], x, M1, K1, 4, y=y)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    launches(500, False)
+    hot = launches(2000, False)
+    launches(R1, True)
+    cold = launches(R1, True)
+    out["C1_gemv_256x512_fp32"] = {"us_per_launch_hot": hot * 1e6, "us_per_launch_cold": cold * 1e6,
+                                   "weights_per_s_cold": M1 * K1 / cold, "cold_copies": R1}
+    del seeds, coefs, codes, mats
+    # C2: one expert, top-1 with weight 1 (graph replays)
+    b2 = synth.config_seed(1)
+    ex = {n: to_dev(synth.seed_matrix(b2, f"bench.C2.{n}", *((768, 2048) if n != "down" else (2048, 768)), 4, 1))
+          for n in ("gate", "up", "down")}
+    c2 = {}
+    for T2 in (1, 8):
+        ids = torch.zeros((T2, 1), dtype=torch.int32, device=dev)
+        w = torch.ones((T2, 1), dtype=torch.float32, device=dev)
+        xs = [torch.from_numpy(synth.bf16_bits(synth.normal_f32(b2, f"bench.C2.x{T2}.{g}", (T2, 2048))).view(np.int16)
+                               ).view(torch.bfloat16).to(dev) for g in range(4)]
+        y2 = torch.empty((T2, 2048), dtype=torch.float32, device=dev)
+        ws = torch.empty(seedmm.moe_workspace_bytes(T2, 1, 1, 2048, 768), dtype=torch.uint8, device=dev)
+        calls = [lambda xg=xg: seedmm.moe(ids, w, xg, 1, 2048, 768, 4, ex["gate"], ex["up"], ex["down"],
+                                          y=y2, workspace=ws) for xg in xs]
+        t = graph_step(torch, calls, 200)
+        c2[f"T{T2}_us"] = t * 1e6
+        c2[f"T{T2}_weights_per_s"] = 3 * 2048 * 768 / t
+    out["C2_expert_2048x768_P4"] = c2
+    del ex
+    # C4: the 100-expert layer with P = 3
+    b4 = synth.config_seed(3)
+    l3 = [{n: to_dev(synth.seed_matrix(b4, n, *((I, H) if n != "down" else (H, I)), 3, E))
+           for n in ("gate", "up", "down")}]
+    for _ in range(2):
+        l3.append({n: {k: v.clone() for k, v in mm.items()} for n, mm in l3[0].items()})
+    c4 = {}
+    for T4 in (1, 16):
+        calls, dist = [], []
+        y4 = torch.empty((T4, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(seedmm.moe_workspace_bytes(T4, TOPK, E, H, I), dtype=torch.uint8, device=dev)
+        for g in range(6):
+            ids, w = synth.route_topk(b4, f"bench.C4.r{T4}.{g}", T4, E, TOPK)
+            dist.append(len(np.unique(ids)))
+            xg = torch.from_numpy(synth.bf16_bits(synth.normal_f32(b4, f"bench.C4.x{T4}.{g}", (T4, H))).view(np.int16)
+                                  ).view(torch.bfloat16).to(dev)
+            r = l3[g % 3]
+            calls.append(lambda i=torch.from_numpy(ids).to(dev), wt=torch.from_numpy(w).to(dev), xg=xg, r=r:
+                         seedmm.moe(i, wt, xg, E, H, I, 3, r["gate"], r["up"], r["down"], y=y4, workspace=ws))
+        t = graph_step(torch, calls, 100 if T4 == 1 else 50)
+        c4[f"T{T4}_us"] = t * 1e6
+        c4[f"T{T4}_weights_per_s"] = np.mean(dist) * 3 * H * I / t
+        c4[f"T{T4}_tok_s"] = T4 / t
+    out["C4_moe_layer_P3"] = c4
+    del l3
+    # C5: 4096-token prefill through the P = 4 layer (the headline's weight copies)
+    T5 = 4096
+    y5 = torch.empty((T5, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(seedmm.moe_workspace_bytes(T5, TOPK, E, H, I), dtype=torch.uint8, device=dev)
+    b5 = synth.config_seed(2)
+    calls = []
+    for g in range(3):
+        ids, w = synth.route_topk(b5, f"bench.C5.r{g}", T5, E, TOPK)
+        xg = torch.from_numpy(synth.bf16_bits(synth.normal_f32(b5, f"bench.C5.x{g}", (T5, H))).view(np.int16)
+                              ).view(torch.bfloat16).to(dev)
+        r = reps[g % len(reps)]
+        calls.append(lambda i=torch.from_numpy(ids).to(dev), wt=torch.from_numpy(w).to(dev), xg=xg, r=r:
+                     seedmm.moe(i, wt, xg, E, H, I, 4, r["gate"], r["up"], r["down"], y=y5, workspace=ws))
+    t = graph_step(torch, calls, 10)
+    flops = 2.0 * T5 * TOPK * 3 * H * I
+    out["C5_prefill_T4096_P4"] = {"ms_per_step": t * 1e3, "tok_s": T5 / t,
+                                  "weights_per_s": E * 3 * H * I / t,
+                                  "mfma_tflops": flops / t / 1e12, "mfma_frac": flops / t / MFMA_PEAK}
+    return out
 
 
 def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, steps=30):
@@ -527,6 +655,9 @@ def main():
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
                               "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6}
         out["by_batch"] = sweep
+
+    if not args.no_configs:
+        out["configs"] = config_lines(torch, seedmm, synth, reps, to_dev)
 
     if not args.no_mixed:
         out["mixed"] = mixed_bench(torch, seedmm, synth, dev, T, args.replicas, to_dev)
