@@ -182,10 +182,11 @@ def graph_step(torch, calls, steps):
     return t
 
 
-def config_lines(torch, seedmm, synth, reps, to_dev):
+def config_lines(torch, seedmm, synth, reps, to_dev, P):
     """One timed figure for each of the other workloads: the single matrix-vector product
     (256 x 512, fp32 x), one SwiGLU expert (2048 -> 768 -> 2048) at 1 and 8 tokens, the
-    P = 3 layer at 1 and 16 tokens, and 4096-token prefill through the P = 4 layer."""
+    P = 3 layer at 1 and 16 tokens, and 4096-token prefill through the bench's own layer
+    (`reps`, whose streams have P coefficients per block)."""
     dev = torch.device("cuda:0")
     out = {}
     # C1: back-to-back launches on the default stream (launch overhead included), on one
@@ -260,7 +261,7 @@ def config_lines(torch, seedmm, synth, reps, to_dev):
         c4[f"T{T4}_tok_s"] = T4 / t
     out["C4_moe_layer_P3"] = c4
     del l3
-    # C5: 4096-token prefill through the P = 4 layer (the headline's weight copies)
+    # C5: 4096-token prefill through the headline's layer (its weight copies, its P)
     T5 = 4096
     y5 = torch.empty((T5, H), dtype=torch.float32, device=dev)
     ws = torch.empty(seedmm.moe_workspace_bytes(T5, TOPK, E, H, I), dtype=torch.uint8, device=dev)
@@ -272,10 +273,10 @@ def config_lines(torch, seedmm, synth, reps, to_dev):
                               ).view(torch.bfloat16).to(dev)
         r = reps[g % len(reps)]
         calls.append(lambda i=torch.from_numpy(ids).to(dev), wt=torch.from_numpy(w).to(dev), xg=xg, r=r:
-                     seedmm.moe(i, wt, xg, E, H, I, 4, r["gate"], r["up"], r["down"], y=y5, workspace=ws))
+                     seedmm.moe(i, wt, xg, E, H, I, P, r["gate"], r["up"], r["down"], y=y5, workspace=ws))
     t = graph_step(torch, calls, 10)
     flops = 2.0 * T5 * TOPK * 3 * H * I
-    out["C5_prefill_T4096_P4"] = {"ms_per_step": t * 1e3, "tok_s": T5 / t,
+    out[f"C5_prefill_T4096_P{P}"] = {"ms_per_step": t * 1e3, "tok_s": T5 / t,
                                   "weights_per_s": E * 3 * H * I / t,
                                   "mfma_tflops": flops / t / 1e12, "mfma_frac": flops / t / MFMA_PEAK}
     return out
@@ -306,7 +307,7 @@ def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, steps=30):
     def call(g):
         r = reps[g % len(reps)]
         seedmm.moe_mixed(ids_l[g], w_l[g], x_l[g], E, H, I, mask, r["gate"], r["up"], r["down"],
-                         y=y, workspace=ws)
+                         y=y, workspace=ws, Ps=Ps)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -657,7 +658,7 @@ def main():
         out["by_batch"] = sweep
 
     if not args.no_configs:
-        out["configs"] = config_lines(torch, seedmm, synth, reps, to_dev)
+        out["configs"] = config_lines(torch, seedmm, synth, reps, to_dev, P)
 
     if not args.no_mixed:
         out["mixed"] = mixed_bench(torch, seedmm, synth, dev, T, args.replicas, to_dev)

@@ -122,13 +122,47 @@ def _mat(m: dict):
     return m
 
 
+def stream_sizes(E: int, M: int, K: int, Ps) -> dict:
+    """Elements of the seeds (u16), coefs (u16) and codes (u8) streams of E stacked [M][K]
+    matrices; Ps is one P for all, or a P per matrix (mixed packs)."""
+    n = M * (K // 8)
+    Ps = [int(Ps)] * E if isinstance(Ps, int) else [int(p) for p in Ps]
+    if len(Ps) != E:
+        raise ValueError(f"{len(Ps)} values of P for {E} matrices")
+    coef_nibbles = sum(n * p for p in Ps)
+    return {"seeds": E * n, "coefs": (coef_nibbles + 3) // 4, "codes": (E * n + 1) // 2}
+
+
+def _check_streams(m: dict, E: int, M: int, K: int, Ps, name: str, exact_coefs=True):
+    """The kernels index the streams from (E, M, K, P) alone: a stream shorter than that
+    would be read out of bounds, so it is refused here, before anything is launched."""
+    need = stream_sizes(E, M, K, Ps)
+    for k, n in need.items():
+        if not exact_coefs and k == "coefs":
+            continue
+        if m[k].numel() < n:
+            raise ValueError(f"{name}.{k} has {m[k].numel()} elements; {E} stacked {M}x{K} "
+                             f"matrices need {n}")
+    eb = m.get("exp_bias")
+    if isinstance(eb, torch.Tensor) and eb.numel() < E:
+        raise ValueError(f"{name}.exp_bias has {eb.numel()} entries for {E} matrices")
+
+
+def _check_numel(t, n, name):
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, {n} needed")
+
+
 def gemv(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor = None):
     """y = W x for fp32 x[K] (seedmm_gemv, default stream)."""
     _mat(mat)
+    _check_streams(mat, 1, M, K, P, "W")
     _dev(x, torch.float32, "x")
+    _check_numel(x, K, "x")
     if y is None:
         y = torch.empty(M, dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
+    _check_numel(y, M, "y")
     eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
     _check(_lib.seedmm_gemv(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
                             _ptr(x), _ptr(y), M, K, P), "seedmm_gemv")
@@ -142,11 +176,16 @@ def gemv_ex(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor 
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("x must be float32 or bfloat16")
     _dev(x, x.dtype, "x")
+    _check_streams(mat, 1, M, K, P, "W")
     N = x.shape[0] if x.dim() == 2 else 1
     ldx = x.shape[-1]
+    if ldx < K:
+        raise ValueError(f"x rows hold {ldx} elements, K = {K}")
     if y is None:
         y = torch.empty((N, M), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
+    if y.shape[-1] < M or y.numel() < N * y.shape[-1]:
+        raise ValueError(f"y must hold [{N}][{M}]")
     eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
     _check(_lib.seedmm_gemv_ex(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
                                _ptr(x), F32 if x.dtype == torch.float32 else BF16, ldx, _ptr(y),
@@ -157,10 +196,12 @@ def gemv_ex(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor 
 def reconstruct(mat: dict, M: int, K: int, P: int, dtype=torch.float32, out=None, stream=None):
     """W[M][K] in fp32 (exact) or bf16 (seedmm_reconstruct)."""
     _mat(mat)
+    _check_streams(mat, 1, M, K, P, "W")
     dev = mat["seeds"].device
     if out is None:
         out = torch.empty((M, K), dtype=dtype, device=dev)
     _dev(out, dtype, "W")
+    _check_numel(out, M * K, "W")
     eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
     _check(_lib.seedmm_reconstruct(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
                                    _ptr(out), F32 if dtype == torch.float32 else BF16, M, K, P,
@@ -190,6 +231,13 @@ def _seedmat(m: dict) -> SeedMat:
                    m["exp_bias"].data_ptr())
 
 
+def _check_layer(T, k, topk_w, x, E, H, I, Ps, gate, up, down, exact_coefs=True):
+    _check_numel(topk_w, T * k, "topk_w")
+    _check_numel(x, T * H, "x")
+    for name, m, (M, K) in (("gate", gate, (I, H)), ("up", up, (I, H)), ("down", down, (H, I))):
+        _check_streams(m, E, M, K, Ps, name, exact_coefs)
+
+
 def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None, stream=None,
         events=None):
     """Routed SwiGLU MoE layer (seedmm_moe); x bf16 [T][H] -> y fp32 [T][H].
@@ -199,9 +247,11 @@ def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None,
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")
     T, k = topk_ids.shape
+    _check_layer(T, k, topk_w, x, E, H, I, P, gate, up, down)
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
+    _check_numel(y, T * H, "y")
     need = moe_workspace_bytes(T, k, E, H, I)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -230,14 +280,18 @@ def p4_mask(Ps, device) -> torch.Tensor:
 
 
 def moe_mixed(topk_ids, topk_w, x, E, H, I, p4mask, gate, up, down, y=None, workspace=None,
-              stream=None):
+              stream=None, Ps=None):
     """Routed SwiGLU MoE layer with P chosen per expert (seedmm_moe_mixed); p4mask from
-    p4_mask()."""
+    p4_mask(Ps).  Given Ps, the coefficient streams are checked against it; without, only
+    the seed and code streams are (the mask lives on the device)."""
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")
     _dev(p4mask, torch.int32, "p4mask")
+    _check_numel(p4mask, (E + 31) // 32, "p4mask")
     T, k = topk_ids.shape
+    _check_layer(T, k, topk_w, x, E, H, I, Ps if Ps is not None else 3, gate, up, down,
+                 exact_coefs=Ps is not None)
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
@@ -258,6 +312,9 @@ def search(W: torch.Tensor, P: int, exp_bias: int, colw: torch.Tensor = None, er
     err (float64 [M*K/8], squared error of every block)."""
     _dev(W, torch.float32, "W")
     M, K = W.shape
+    if colw is not None:
+        _dev(colw, torch.float32, "colw")
+        _check_numel(colw, K, "colw")
     nblk = M * (K // 8)
     dev = W.device
     out = {"seeds": torch.empty(nblk, dtype=torch.uint16, device=dev),
@@ -293,6 +350,14 @@ class ExpertCache:
         if rec == 0 or nstate == 0 or ndev == 0:
             raise SeedmmError(EINVAL, "seedmm_cache sizes")
         self.record_bytes = rec
+        for n, (M, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            need = stream_sizes(E, M, K, P)
+            for part, cnt in need.items():
+                if np.asarray(host[n][part]).size < cnt:
+                    raise ValueError(f"{n}.{part} has {np.asarray(host[n][part]).size} "
+                                     f"elements; {E} stacked {M}x{K} matrices need {cnt}")
+            if np.asarray(host[n]["exp_bias"]).size < E:
+                raise ValueError(f"{n}.exp_bias has fewer than {E} entries")
         pack = torch.zeros(E * rec, dtype=torch.uint8, pin_memory=True)
         view = pack.numpy().reshape(E, rec)
         for m, n in enumerate(("gate", "up", "down")):

@@ -135,3 +135,38 @@ def test_moe_mixed_rejects_a_missing_mask(lib):
     m = SeedMat(FAKE, FAKE, FAKE, FAKE)
     assert lib.seedmm_moe_mixed(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 64, 64, None, m, m, m,
                                 FAKE, 1 << 30, None) == -1
+
+
+def test_binding_stream_sizes_match_the_generated_streams():
+    """The binding's length check uses the stream sizes the layout fixes: they equal the
+    lengths of generated stacks, uniform and mixed."""
+    import numpy as np
+    import synth
+    from pseudo_random_weight_amd import seedmm
+    for (E, M, K, P) in [(1, 256, 512, 4), (3, 24, 16, 3), (5, 64, 128, 4)]:
+        m = synth.seed_matrix(synth.config_seed(0), f"sz{E}{P}", M, K, P, E)
+        need = seedmm.stream_sizes(E, M, K, P)
+        assert need == {k: m[k].size for k in ("seeds", "coefs", "codes")}
+    Ps = [4, 3, 3, 4, 3]
+    mm = synth.seed_matrix_mixed(synth.config_seed(0), "szmix", 32, 64, Ps)
+    assert seedmm.stream_sizes(5, 32, 64, Ps) == {k: mm[k].size for k in ("seeds", "coefs", "codes")}
+
+
+def test_binding_refuses_short_streams():
+    """A P = 3 stack passed as P = 4 (its coefficient stream is a quarter short) is refused
+    before any launch, as is a missing expert."""
+    import numpy as np
+    import torch
+    import synth
+    from pseudo_random_weight_amd import seedmm
+    E, M, K = 4, 32, 64
+    m3 = synth.seed_matrix(synth.config_seed(0), "short", M, K, 3, E)
+    t = {k: torch.from_numpy(np.ascontiguousarray(m3[k]).view(np.uint8 if k == "codes" else np.int16))
+         for k in ("seeds", "coefs", "codes")}
+    t["exp_bias"] = torch.from_numpy(m3["exp_bias"])
+    seedmm._check_streams(t, E, M, K, 3, "gate")                  # fits
+    with pytest.raises(ValueError, match="coefs"):
+        seedmm._check_streams(t, E, M, K, 4, "gate")
+    with pytest.raises(ValueError, match="seeds"):
+        seedmm._check_streams(t, E + 1, M, K, 3, "gate")
+    seedmm._check_streams(t, E, M, K, 4, "gate", exact_coefs=False)   # mixed without Ps

@@ -511,7 +511,7 @@ def _run_mixed(sm, mats, Ps, ids, w, x, E, H, I):
     xt, x32 = bf16_tensor(x)
     mask = sm.p4_mask(Ps, "cuda")
     y = sm.moe_mixed(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), xt, E, H, I, mask,
-                     *[dev(m) for m in mats])
+                     *[dev(m) for m in mats], Ps=Ps)
     torch.cuda.synchronize()
     return y.cpu().numpy(), x32
 
