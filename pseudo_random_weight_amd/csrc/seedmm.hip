@@ -582,13 +582,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ f32x4 red[4][1][64];
     __shared__ uint32_t tab[512];
     extern __shared__ uint4 xs[];
+    // the expert id, the activation row and the tables do not depend on each other: the
+    // row's loads and the table fill run while the id is in flight
     const int e = a.ids[blockIdx.y];
-    if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
-    if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
     const int64_t row = MODE == MODE_GATEUP ? 0 : (int64_t)blockIdx.y;
     const uint4* src = (const uint4*)(a.x + row * a.ldx);
     for (int i = threadIdx.x; i < a.K / 8; i += 256) xs[i] = src[i];
     fill_lfsr_tables(tab);   // its barrier also publishes xs
+    if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
+    if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
     mfma_run<P, VEC, 1, MODE, true, RT, true>(a, e, 1, kSlotIota + blockIdx.y, tab, red,
                                               (const uint16_t*)xs);
 }
