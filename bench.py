@@ -654,7 +654,10 @@ def main():
             sweep[str(Ts)] = {"ms_per_step": ts * 1e3, "tok_s": Ts / ts,
                               "weights_per_s": dis.mean() * 3 * w_per_mat / ts,
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
-                              "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6}
+                              "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6,
+                              # event timing: includes a few microseconds of event records
+                              "gate_up_valu_frac": dis.mean() * 2 * w_per_mat * (2 * P + 1)
+                              / st[1] / VALU_PEAK}
         out["by_batch"] = sweep
 
     if not args.no_configs:
