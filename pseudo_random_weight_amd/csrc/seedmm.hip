@@ -1251,7 +1251,9 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     b.M = H; b.K = I;
     b.x = hbuf; b.ldx = I;
     b.counts = counts; b.lists = lists; b.E = E; b.T = T; b.top_k = top_k;
-    b.topk_w = topk_w; b.y = obuf; b.ldy = H;
+    // top-1 routing: the per-slot outputs are y itself (the combine of one slot copies it)
+    const bool direct = top_k == 1;
+    b.topk_w = topk_w; b.y = direct ? y : obuf; b.ldy = H;
     b.ids = a.ids;
     b.p4mask = p4mask;
     b.slot = slot;
@@ -1259,9 +1261,11 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
     mark(3);
 
-    const int64_t n4 = (int64_t)T * (H / 4);
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, obuf,
-                       top_k, y, H, T);
+    if (!direct) {
+        const int64_t n4 = (int64_t)T * (H / 4);
+        hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                           obuf, top_k, y, H, T);
+    }
     mark(4);
     return launch_status();
 }
