@@ -7,7 +7,8 @@
  * matrix holds one int32 exp_bias (model card "K2-Horizon-MoVA-36B-A4B - NanoSeedLM
  * p4mx-q4v", section "This upload": NAME.seeds U16, NAME.coefs U16, NAME.codes U8,
  * NAME.exp_bias I32).  The kernels regenerate each block inside the product and never
- * write W back (NanoSeedLM README, "Highlights"; barnson.org post, "Never decompress"):
+ * write W back (NanoSeedLM README, "Highlights"; barnson.org post, "What I changed:
+ * September 2026", never decompress):
  *
  *     w_i = 2^(code + exp_bias - 15) * sum_{j<P} c_j * (s_{iP+j+1} - 32768),  i = 0..7
  *

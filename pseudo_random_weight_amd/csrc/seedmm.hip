@@ -3,7 +3,7 @@
 // Every kernel regenerates the weight blocks it needs from (seed, coefficients,
 // exponent code) in registers and consumes them at once; no kernel but
 // seedmm_reconstruct writes a weight to memory (NanoSeedLM README, "Highlights";
-// barnson.org post, "Never decompress").
+// barnson.org post, "What I changed: September 2026", never decompress).
 //
 // Work mapping shared by the product kernels.  A wave owns 16 rows of one matrix.
 // Lane l = r + 16 q (r = l % 16, q = l / 16) decodes blocks of row r in runs of 8
@@ -306,7 +306,7 @@ struct MfmaArgs {
     seedmm_mat A;           // gate (GATEUP) or the matrix
     seedmm_mat A2;          // up (GATEUP)
     int exp_bias;           // GEMM: scalar exp_bias
-    int M, K, P_unused;
+    int M, K;               // rows and columns of one matrix
     const uint16_t* x;      // GEMM/GATEUP: activations bf16 [.][ldx]; DOWN: h [.][ldx]
     int ldx;
     int N;                  // GEMM: number of rows of x
