@@ -523,8 +523,8 @@ __device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, cons
 // Mixed packs (a.p4mask set) run one launch per P; each launch serves only the experts
 // of its own P.  (One launch holding both bodies was slower: the two bodies shared one
 // register allocation and the P = 3 loop came out scheduled worse than in its own kernel.)
-// Register budget: 5 waves per SIMD for P = 4 and 6 for P = 3 (measured against 4, 5
-// and 6: a tighter budget spills in P = 4 gate/up, a looser one hides fewer stalls).
+// Register budget: 5 waves per SIMD for P = 4 and 6 for P = 3, the fastest of 4, 5 and 6
+// measured (6 makes P = 4 gate/up spill; 4 leaves fewer waves to hide load latency).
 template <int P, bool VEC, int NT, int MODE, bool TAB, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (P == 4 ? 5 : 6) : 2))) void k_mfma(const MfmaArgs a) {
     static_assert(MODE != MODE_GATEUP || RT == 1, "gate/up pairs its waves by matrix");
