@@ -14,6 +14,9 @@
  *             "GPU search == CPU search".
  *   [INDEX]   NanoSeedLM documentation index page, sections "Results" and "Plans".
  *
+ * Parity unpinned: the register's tap mask and the basis fill order are readings; the
+ * pages print no seed -> weights example to check them against.
+ *
  * Build: cc -O2 -std=c99 -ffp-contract=off -fopenmp -shared -fPIC seedref.c -lm
  */
 #include "seedref.h"

@@ -24,8 +24,9 @@
  *   - block b of an [M][K] matrix covers row m = b / (K/8), columns 8*(b % (K/8)) ...
  *
  * Parity status: every function here is pinned by CPU tests against closed forms,
- * exhaustive invariants, brute force and library reductions; the fill order and the
- * tap mask are readings and cannot be pinned against the published model files.
+ * exhaustive invariants, brute force and library reductions.  Parity unpinned: the
+ * fill order and the tap mask are readings, and bit-compatibility with the published
+ * model files cannot be checked (the pages print no seed -> weights example).
  *
  * Floating point: built with -ffp-contract=off; products accumulate in double.
  */
