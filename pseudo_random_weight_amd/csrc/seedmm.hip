@@ -599,20 +599,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // Wide-token products (prefill and long token lists), vector-load layouts only
 // (K % 256 == 0, 16-byte aligned streams).  A workgroup of 8 waves owns AR = 128 weight
 // rows (64 rows of gate and of up, or 128 rows of one matrix) for up to NC = 384 tokens,
-// so each weight block is regenerated once per pass over its expert's tokens.
-// Per 32-k step (blocks 4s..4s+3 of every row, contiguous k):
-//   - each thread regenerates one block and writes its 8 bf16 weights to LDS (A tile);
-//   - the step's 64-byte slice of every token row is staged in LDS (B tile);
-//   - wave w = (row half rh, token quarter tq) multiplies its two 32-row A tiles (gate
-//     and up rows of one half, or two row tiles) with its three 32-token tiles on
-//     v_mfma_f32_32x32x16_bf16 (two k halves per step), accumulators in registers.
+// so each weight block is regenerated once per pass over its expert's tokens.  The waves
+// split by role, one of each role on every SIMD, so that a SIMD's vector ALU and its
+// matrix core work at the same time:
+//   - producers (waves 0-3) regenerate the A tile of the next 32-k step (two blocks per
+//     lane) and stage its B tile (the step's 64-byte slice of every token row), both in
+//     LDS;
+//   - consumers (waves 4-7), wave (row half rh, token half th), multiply their two 32-row
+//     A tiles (gate and up rows of one half, or two row tiles) with six 32-token B tiles
+//     on v_mfma_f32_32x32x16_bf16 (two k halves per step), accumulators in registers,
+//     and write the results.
 // LDS tiles are stored per k half ([half][row or token][2 blocks][8 bf16]) so every MFMA
-// fragment is one contiguous 1 KB read.  A and B are double-buffered; the vector ALUs
-// regenerate step s+1 while the matrix cores work on step s.  Each thread's stream values
-// for step s+2 are read into registers during step s, so regeneration starts right after
-// the barrier.  The seed / coefficient / code streams of each 32-block group are staged
-// in LDS with 16-byte loads a group ahead; a row's stream chunks are written and read by
-// the four lanes of one quad (same-wave LDS order, no barrier needed).
+// fragment is one contiguous 1 KB read.  A and B are double-buffered: the producers fill
+// step s+1 while the consumers multiply step s, with one barrier per step.  During step s
+// a producer also reads its stream values for step s+2 and issues step s+2's B loads.
+// The seed / coefficient / code streams of each 32-block group are staged in LDS with
+// 16-byte loads a group ahead; a row's chunks are written and read by four lanes of one
+// wave (same-wave LDS order, no barrier needed).
+// Lane l of producer wave w takes rows 16 w + (l & 15) and 64 + 16 w + (l & 15) and
+// 16-byte piece l >> 4 (token slots likewise), so each 16-lane group of a tile store
+// writes 256 contiguous bytes and the stores are free of LDS bank conflicts.
 // Workgroups are numbered so that every row group of one expert lands on the same XCD
 // (workgroups are dealt to the 8 XCDs round-robin), keeping that expert's token rows in
 // one L2.
@@ -620,14 +626,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int P, int MODE>
-__global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
+__global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
     constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;
     constexpr int AR = 128;                   // A rows per workgroup
     constexpr int RM = AR / NMAT;             // rows per matrix
-    constexpr int NTW = 3;                    // 32-token tiles per wave
+    constexpr int NTW = 3;                    // 32-token tiles per consumer wave
     constexpr int NC = 4 * NTW * 32;          // token slots per pass (384)
+    constexpr int NBU = NC * 4 / 512;         // B pieces per producer lane and step (3)
     constexpr int SROW = 40;                  // staged stream row stride in u16 (80 B: the
-                                              // 16 rows a wave reads start in distinct banks)
+                                              // 16 rows a lane group reads start in distinct banks)
     __shared__ u32x4 As[2][2 * AR * 2];
     __shared__ u32x4 Bs[2][2 * NC * 2];
     __shared__ uint16_t Ss[2][AR * SROW];
@@ -637,10 +644,9 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     fill_lfsr_tables(tab);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, lh = lane >> 5;
-    const int rh = wave >> 2, tq = wave & 3;
-    const bool vfirst = __builtin_amdgcn_readfirstlane(rh) == 0;   // wave-uniform
+    const bool producer = wave < 8;           // wave-uniform
 
     // ---- XCD-aware numbering: consecutive work items share an XCD ------------------
     const int total = gridDim.x * gridDim.y;
@@ -682,213 +688,203 @@ __global__ __launch_bounds__(512, 1) void k_wide(const MfmaArgs a) {
     const int ngroups = nbpr / 32;            // K % 256 == 0
     const int NS = ngroups * 8;
 
-    // this wave's two A tiles (32 A-rows each): gate and up rows of half rh, or 2rh, 2rh+1
-    const int ta0 = NMAT == 2 ? rh : 2 * rh;
-    const int ta1 = NMAT == 2 ? 2 + rh : 2 * rh + 1;
-
-    // ---- regeneration role: A row `arow` (matrix dmat, row drow), block lane dj ------
-    const int arow = tid >> 2, dj = tid & 3;
-    const int dmat = arow / RM, drow = arow % RM;
-    Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
-    if constexpr (NMAT == 2) {
-        if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask, a.slot, a.slot_stride);
-    }
-    const bool drv = m0 + drow < M;
-    const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
-    // LDS tile layout [k half][32-row group][block in half][32 rows]: a half-wave's
-    // fragment read is 512 contiguous bytes (no bank conflicts)
-    const int a_slot = ((dj >> 1) * AR + (arow & ~31)) * 2 + (dj & 1) * 32 + (arow & 31);
-
-    u32x4 sreg_s, sreg_c, sreg_d;
-    auto stream_load = [&](int g) {
-        const int64_t b0 = drowb + 32 * g;    // first block of the group in this row
-        sreg_s = *reinterpret_cast<const u32x4*>(W.seeds + b0 + 8 * dj);
-        if (dj < P) sreg_c = *reinterpret_cast<const u32x4*>(W.coefs + (b0 * P) / 4 + 8 * dj);
-        if (dj == 0) sreg_d = *reinterpret_cast<const u32x4*>(W.codes + b0 / 2);
-    };
-    auto stream_store = [&](int buf) {
-        *reinterpret_cast<u32x4*>(&Ss[buf][arow * SROW + 8 * dj]) = sreg_s;
-        // missing rows get zero coefficients (zero weights); applied here, not at the
-        // load, so the load is not waited for early
-        if (dj < P)
-            *reinterpret_cast<u32x4*>(&Cs[buf][arow * SROW + 8 * dj]) =
-                drv ? sreg_c : u32x4{0u, 0u, 0u, 0u};
-        if (dj == 0) *reinterpret_cast<u32x4*>(&Ds[buf][arow * 16]) = sreg_d;
-    };
-    struct Blk { uint32_t seed, cw, code; };
-    auto fetch = [&](int s) {
-        const int buf = (s >> 3) & 1;
-        const int bl = 4 * (s & 7) + dj;      // block within the group
-        Blk k;
-        k.seed = Ss[buf][arow * SROW + bl];
-        if constexpr (P == 4) {
-            k.cw = Cs[buf][arow * SROW + bl];
-        } else {
-            const int n = 3 * bl, sh = 4 * (n & 3);
-            const uint16_t* c = &Cs[buf][arow * SROW + (n >> 2)];
-            k.cw = ((uint32_t)c[0] | ((uint32_t)c[1] << 16)) >> sh;
+    if (producer) {
+        // ---- producer: A row r (matrix dmat, row drow), 16-byte piece dj --------------
+        const int dj = lane >> 4;
+        const int r = 16 * wave + (lane & 15);
+        const int dmat = r / RM, drow = r % RM;
+        Mat W = mat_of(a.A, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
+        if constexpr (NMAT == 2) {
+            if (dmat == 1) W = mat_of(a.A2, e, nblk, P, 0, true, a.p4mask, a.slot, a.slot_stride);
         }
-        k.code = ((uint32_t)Ds[buf][arow * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
-        return k;
-    };
-    auto regen = [&](const Blk& k, u32x4* dst) {
-        float w[8];
-        decode_block<P>(window_from_tables(k.seed, tab), k.cw, k.code, W.exp_bias, w);
-        *dst = __builtin_bit_cast(u32x4, pack_bf16(w));
-    };
+        const bool drv = m0 + drow < M;
+        const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
+        // LDS tile layout [k half][32-row group][block in half][32 rows]: a half-wave's
+        // fragment read is 512 contiguous bytes (no bank conflicts)
+        const int a_slot = ((dj >> 1) * AR + (r & ~31)) * 2 + (dj & 1) * 32 + (r & 31);
 
-    for (int pass = 0; pass < n_e; pass += NC) {
-        // B staging role: chunks tid + 512 u = (token slot, 16-byte piece dj)
-        const uint16_t* brow[NTW];
-        int bslot[NTW];
-#pragma unroll
-        for (int u = 0; u < NTW; ++u) {
-            const int ts = (tid + 512 * u) >> 2;
-            const int i = min(pass + ts, n_e - 1);
-            int64_t src;
-            if constexpr (MODE == MODE_GEMM) src = i;
-            else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
-            else src = list[i];
-            brow[u] = a.x + src * a.ldx + 8 * dj;
-            bslot[u] = ((dj >> 1) * NC + (ts & ~31)) * 2 + (dj & 1) * 32 + (ts & 31);
-        }
-
-        f32x16 acc[2][NTW];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int t = 0; t < NTW; ++t)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[x][t][v] = 0.f;
-
-        // prologue: group 0 staged, group 1 in registers; step 0's weights and B slice in
-        // buffer 0, step 1's B slice in flight, step 1's stream values in registers.
-        stream_load(0);
-        stream_store(0);
-        if (ngroups > 1) stream_load(1);
-        u32x4 bA[NTW], bB[NTW];               // two register sets, named statically
-#pragma unroll
-        for (int u = 0; u < NTW; ++u) bA[u] = *reinterpret_cast<const u32x4*>(brow[u]);
-#pragma unroll
-        for (int u = 0; u < NTW; ++u) bB[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32);
-        regen(fetch(0), &As[0][a_slot]);
-        Blk nxt = fetch(1);
-#pragma unroll
-        for (int u = 0; u < NTW; ++u) Bs[0][bslot[u]] = bA[u];
-        __syncthreads();
-
-// One 32-k step s, straight-line.  The vector ALUs start at once on step s+1's weights
-// (stream values already in registers), then fetch step s+2's stream values (storing the
-// next group's streams when s+2 opens it) and issue step s+2's B loads; the matrix cores
-// work on buffer s&1 meanwhile.  Step s+1's weights and B slice (BSTORE) go to buffer
-// s&1^1.  Indices past the last step are clamped; those writes land in buffers nobody
-// reads.
-#define SEEDMM_WIDE_REGEN(S, BNEXT)                                                          \
-    {                                                                                        \
-        const int s_ = (S);                                                                  \
-        regen(nxt, &As[(s_ & 1) ^ 1][a_slot]);                                               \
-        if (((s_ + 2) & 7) == 0 && s_ + 2 < NS) {                                            \
-            const int g2 = (s_ + 2) >> 3;                                                    \
-            stream_store(g2 & 1);                                                            \
-            if (g2 + 1 < ngroups) stream_load(g2 + 1);                                       \
-        }                                                                                    \
-        nxt = fetch(min(s_ + 2, NS - 1));                                                    \
-        const int snext = min(s_ + 2, NS - 1);                                               \
-        _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                      \
-            BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * snext);                \
-    }
-#define SEEDMM_WIDE_MFMA(S)                                                                  \
-    {                                                                                        \
-        const int buf = (S) & 1;                                                             \
-        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                      \
-            const bf16x8 A0 =                                                                \
-                __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta0) * 2 + lane]);         \
-            const bf16x8 A1 =                                                                \
-                __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta1) * 2 + lane]);         \
-            _Pragma("unroll") for (int t = 0; t < NTW; ++t) {                                \
-                const bf16x8 Bf = __builtin_bit_cast(                                        \
-                    bf16x8, Bs[buf][(h * NC + 32 * (tq * NTW + t)) * 2 + lane]);             \
-                acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, Bf, acc[0][t], 0, 0, 0); \
-                acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, Bf, acc[1][t], 0, 0, 0); \
-            }                                                                                \
-        }                                                                                    \
-    }
-// Waves 0-3 regenerate first and multiply second, waves 4-7 the other way round, so the
-// two waves sharing a SIMD keep its vector ALU and its matrix core busy at the same time.
-#define SEEDMM_WIDE_STEP(S, BNEXT, BSTORE, FIRST, SECOND)                                    \
-    {                                                                                        \
-        FIRST;                                                                               \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
-        SECOND;                                                                              \
-        _Pragma("unroll") for (int u = 0; u < NTW; ++u)                                      \
-            Bs[((S) & 1) ^ 1][bslot[u]] = BSTORE[u];                                         \
-        __syncthreads();                                                                     \
-    }
-        if (vfirst) {
-            for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
-                SEEDMM_WIDE_STEP(s, bA, bB, SEEDMM_WIDE_REGEN(s, bA), SEEDMM_WIDE_MFMA(s))
-                SEEDMM_WIDE_STEP(s + 1, bB, bA, SEEDMM_WIDE_REGEN(s + 1, bB), SEEDMM_WIDE_MFMA(s + 1))
-            }
-        } else {
-            for (int s = 0; s < NS; s += 2) {
-                SEEDMM_WIDE_STEP(s, bA, bB, SEEDMM_WIDE_MFMA(s), SEEDMM_WIDE_REGEN(s, bA))
-                SEEDMM_WIDE_STEP(s + 1, bB, bA, SEEDMM_WIDE_MFMA(s + 1), SEEDMM_WIDE_REGEN(s + 1, bB))
-            }
-        }
-#undef SEEDMM_WIDE_STEP
-#undef SEEDMM_WIDE_MFMA
-#undef SEEDMM_WIDE_REGEN
-
-        // ---- epilogue: lane holds, for token slot 96 tq + 32 t + l32, rows
-        //      8 g + 4 lh + c (g, c = 0..3) of each of its two 32-row tiles -----------
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const int i = pass + 32 * (tq * NTW + t) + l32;
-            if (i >= n_e) continue;
-            int64_t dst;
-            float scale = 1.0f;
-            if constexpr (MODE == MODE_GEMM) {
-                dst = i;
+        u32x4 sreg_s, sreg_c, sreg_d;
+        auto stream_load = [&](int g) {
+            const int64_t b0 = drowb + 32 * g;    // first block of the group in this row
+            sreg_s = *reinterpret_cast<const u32x4*>(W.seeds + b0 + 8 * dj);
+            if (dj < P) sreg_c = *reinterpret_cast<const u32x4*>(W.coefs + (b0 * P) / 4 + 8 * dj);
+            if (dj == 0) sreg_d = *reinterpret_cast<const u32x4*>(W.codes + b0 / 2);
+        };
+        auto stream_store = [&](int buf) {
+            *reinterpret_cast<u32x4*>(&Ss[buf][r * SROW + 8 * dj]) = sreg_s;
+            // missing rows get zero coefficients (zero weights); applied here, not at the
+            // load, so the load is not waited for early
+            if (dj < P)
+                *reinterpret_cast<u32x4*>(&Cs[buf][r * SROW + 8 * dj]) =
+                    drv ? sreg_c : u32x4{0u, 0u, 0u, 0u};
+            if (dj == 0) *reinterpret_cast<u32x4*>(&Ds[buf][r * 16]) = sreg_d;
+        };
+        struct Blk { uint32_t seed, cw, code; };
+        auto fetch = [&](int s) {
+            const int buf = (s >> 3) & 1;
+            const int bl = 4 * (s & 7) + dj;      // block within the group
+            Blk k;
+            k.seed = Ss[buf][r * SROW + bl];
+            if constexpr (P == 4) {
+                k.cw = Cs[buf][r * SROW + bl];
             } else {
-                dst = list[i];
-                if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
+                const int n = 3 * bl, sh = 4 * (n & 3);
+                const uint16_t* c = &Cs[buf][r * SROW + (n >> 2)];
+                k.cw = ((uint32_t)c[0] | ((uint32_t)c[1] << 16)) >> sh;
             }
+            k.code = ((uint32_t)Ds[buf][r * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
+            return k;
+        };
+        auto regen = [&](const Blk& k, u32x4* dst) {
+            float w[8];
+            decode_block<P>(window_from_tables(k.seed, tab), k.cw, k.code, W.exp_bias, w);
+            *dst = __builtin_bit_cast(u32x4, pack_bf16(w));
+        };
+
+        for (int pass = 0; pass < n_e; pass += NC) {
+            // B staging: token slot 16 (wave + 8 u) + (lane & 15), 16-byte piece dj
+            const uint16_t* brow[NBU];
+            int bslot[NBU];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                if constexpr (MODE == MODE_GATEUP) {
-                    const int m = m0 + 32 * rh + 8 * g + 4 * lh;
-                    uint16_t hb[4];
+            for (int u = 0; u < NBU; ++u) {
+                const int ts = 16 * (wave + 8 * u) + (lane & 15);
+                const int i = min(pass + ts, n_e - 1);
+                int64_t src;
+                if constexpr (MODE == MODE_GEMM) src = i;
+                else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
+                else src = list[i];
+                brow[u] = a.x + src * a.ldx + 8 * dj;
+                bslot[u] = ((dj >> 1) * NC + (ts & ~31)) * 2 + (dj & 1) * 32 + (ts & 31);
+            }
+
+            // prologue: group 0 staged, group 1 in registers; step 0's weights and B slice
+            // in buffer 0, step 1's B slice in flight, step 1's stream values in registers
+            stream_load(0);
+            stream_store(0);
+            if (ngroups > 1) stream_load(1);
+            u32x4 bA[NBU], bB[NBU];           // two register sets, named statically
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float gt = acc[0][t][4 * g + c], up = acc[1][t][4 * g + c];
-                        hb[c] = __builtin_bit_cast(uint16_t, (__bf16)(gt / (1.0f + expf(-gt)) * up));
+            for (int u = 0; u < NBU; ++u) bA[u] = *reinterpret_cast<const u32x4*>(brow[u]);
+#pragma unroll
+            for (int u = 0; u < NBU; ++u) bB[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32);
+            regen(fetch(0), &As[0][a_slot]);
+            Blk nxt = fetch(1);
+#pragma unroll
+            for (int u = 0; u < NBU; ++u) Bs[0][bslot[u]] = bA[u];
+            __syncthreads();
+
+// Producer side of step s: step s+1's weights into buffer s&1^1, then the stream values
+// of step s+2 (staging the next group when s+2 opens it), step s+2's B loads, and step
+// s+1's B slice (BSTORE) into buffer s&1^1.  Indices past the last step are clamped;
+// those writes land in buffers nobody reads.
+#define SEEDMM_WIDE_PRODUCE(S, BNEXT, BSTORE)                                                 \
+    {                                                                                         \
+        const int s_ = (S), nb_ = (s_ & 1) ^ 1;                                               \
+        regen(nxt, &As[nb_][a_slot]);                                                         \
+        if (((s_ + 2) & 7) == 0 && s_ + 2 < NS) {                                             \
+            const int g2 = (s_ + 2) >> 3;                                                     \
+            stream_store(g2 & 1);                                                             \
+            if (g2 + 1 < ngroups) stream_load(g2 + 1);                                        \
+        }                                                                                     \
+        const int sn_ = min(s_ + 2, NS - 1);                                                  \
+        nxt = fetch(sn_);                                                                     \
+        _Pragma("unroll") for (int u = 0; u < NBU; ++u)                                       \
+            BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * sn_);                   \
+        _Pragma("unroll") for (int u = 0; u < NBU; ++u) Bs[nb_][bslot[u]] = BSTORE[u];        \
+        __syncthreads();                                                                      \
+    }
+            for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
+                SEEDMM_WIDE_PRODUCE(s, bA, bB)
+                SEEDMM_WIDE_PRODUCE(s + 1, bB, bA)
+            }
+#undef SEEDMM_WIDE_PRODUCE
+            __syncthreads();   // LDS buffers are reused by the next pass
+        }
+    } else {
+        // ---- consumer: wave (rh, tq) --------------------------------------------------
+        const int rh = (wave - 8) >> 2, tq = (wave - 8) & 3;
+        // its two A tiles (32 A-rows each): gate and up rows of half rh, or 2rh, 2rh+1
+        const int ta0 = NMAT == 2 ? rh : 2 * rh;
+        const int ta1 = NMAT == 2 ? 2 + rh : 2 * rh + 1;
+
+        for (int pass = 0; pass < n_e; pass += NC) {
+            f32x16 acc[2][NTW];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int t = 0; t < NTW; ++t)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[x][t][v] = 0.f;
+            __syncthreads();   // the producers' prologue
+
+            for (int s = 0; s < NS; ++s) {
+                const int buf = s & 1;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x8 A0 = __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta0) * 2 + lane]);
+                    const bf16x8 A1 = __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta1) * 2 + lane]);
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) {
+                        const bf16x8 Bf =
+                            __builtin_bit_cast(bf16x8, Bs[buf][(h * NC + 32 * (tq * NTW + t)) * 2 + lane]);
+                        acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, Bf, acc[0][t], 0, 0, 0);
+                        acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, Bf, acc[1][t], 0, 0, 0);
                     }
-                    uint16_t* dp = a.h + dst * a.ldy + m;
-                    if (m + 3 < M && ((uintptr_t)dp & 7) == 0) {
-                        *reinterpret_cast<uint2*>(dp) =
-                            make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
-                    } else {
-                        for (int c = 0; c < 4; ++c)
-                            if (m + c < M) dp[c] = hb[c];
-                    }
+                }
+                __syncthreads();
+            }
+
+            // ---- epilogue: lane holds, for token slot 96 tq + 32 t + l32, rows
+            //      8 g + 4 lh + c (g, c = 0..3) of each of its two 32-row tiles ------------
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+                const int i = pass + 32 * (tq * NTW + t) + l32;
+                if (i >= n_e) continue;
+                int64_t dst;
+                float scale = 1.0f;
+                if constexpr (MODE == MODE_GEMM) {
+                    dst = i;
                 } else {
+                    dst = list[i];
+                    if constexpr (MODE == MODE_DOWN) scale = a.topk_w[dst];
+                }
 #pragma unroll
-                    for (int x = 0; x < 2; ++x) {
-                        const int m = m0 + 32 * (x == 0 ? ta0 : ta1) + 8 * g + 4 * lh;
-                        float* dp = a.y + dst * a.ldy + m;
-                        const f32x4 v = {scale * acc[x][t][4 * g + 0], scale * acc[x][t][4 * g + 1],
-                                         scale * acc[x][t][4 * g + 2], scale * acc[x][t][4 * g + 3]};
-                        if (m + 3 < M && ((uintptr_t)dp & 15) == 0) {
-                            *reinterpret_cast<f32x4*>(dp) = v;
+                for (int g = 0; g < 4; ++g) {
+                    if constexpr (MODE == MODE_GATEUP) {
+                        const int m = m0 + 32 * rh + 8 * g + 4 * lh;
+                        uint16_t hb[4];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float gt = acc[0][t][4 * g + c], up = acc[1][t][4 * g + c];
+                            hb[c] = __builtin_bit_cast(uint16_t, (__bf16)(gt / (1.0f + expf(-gt)) * up));
+                        }
+                        uint16_t* dp = a.h + dst * a.ldy + m;
+                        if (m + 3 < M && ((uintptr_t)dp & 7) == 0) {
+                            *reinterpret_cast<uint2*>(dp) =
+                                make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
                         } else {
                             for (int c = 0; c < 4; ++c)
-                                if (m + c < M) dp[c] = v[c];
+                                if (m + c < M) dp[c] = hb[c];
+                        }
+                    } else {
+#pragma unroll
+                        for (int x = 0; x < 2; ++x) {
+                            const int m = m0 + 32 * (x == 0 ? ta0 : ta1) + 8 * g + 4 * lh;
+                            float* dp = a.y + dst * a.ldy + m;
+                            const f32x4 v = {scale * acc[x][t][4 * g + 0], scale * acc[x][t][4 * g + 1],
+                                             scale * acc[x][t][4 * g + 2], scale * acc[x][t][4 * g + 3]};
+                            if (m + 3 < M && ((uintptr_t)dp & 15) == 0) {
+                                *reinterpret_cast<f32x4*>(dp) = v;
+                            } else {
+                                for (int c = 0; c < 4; ++c)
+                                    if (m + c < M) dp[c] = v[c];
+                            }
                         }
                     }
                 }
             }
+            __syncthreads();   // LDS buffers are reused by the next pass
         }
-        __syncthreads();   // LDS buffers are reused by the next pass
     }
 }
 
@@ -1040,7 +1036,7 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     if (prefill && VEC && a.K % 256 == 0) {
         constexpr int RM = MODE == MODE_GATEUP ? 64 : 128;
         dim3 grid((a.M + RM - 1) / RM, gridy);
-        hipLaunchKernelGGL((k_wide<P, MODE>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((k_wide<P, MODE>), grid, dim3(1024), 0, st, a);
     } else {
         // down and the plain product: two 16-row tiles per workgroup, K in halves
         constexpr int RT = MODE == MODE_GATEUP ? 1 : 2;
