@@ -597,28 +597,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // ----------------------------------------------------------------------------------
 // Wide-token products (prefill and long token lists), vector-load layouts only
-// (K % 256 == 0, 16-byte aligned streams).  A workgroup of 8 waves owns AR = 128 weight
+// (K % 256 == 0, 16-byte aligned streams).  A workgroup of 16 waves owns AR = 128 weight
 // rows (64 rows of gate and of up, or 128 rows of one matrix) for up to NC = 384 tokens,
-// so each weight block is regenerated once per pass over its expert's tokens.  The waves
-// split by role, one of each role on every SIMD, so that a SIMD's vector ALU and its
-// matrix core work at the same time:
-//   - producers (waves 0-3) regenerate the A tile of the next 32-k step (two blocks per
-//     lane) and stage its B tile (the step's 64-byte slice of every token row), both in
-//     LDS;
-//   - consumers (waves 4-7), wave (row half rh, token half th), multiply their two 32-row
-//     A tiles (gate and up rows of one half, or two row tiles) with six 32-token B tiles
-//     on v_mfma_f32_32x32x16_bf16 (two k halves per step), accumulators in registers,
-//     and write the results.
-// LDS tiles are stored per k half ([half][row or token][2 blocks][8 bf16]) so every MFMA
-// fragment is one contiguous 1 KB read.  A and B are double-buffered: the producers fill
-// step s+1 while the consumers multiply step s, with one barrier per step.  During step s
-// a producer also reads its stream values for step s+2 and issues step s+2's B loads.
-// The seed / coefficient / code streams of each 32-block group are staged in LDS with
-// 16-byte loads a group ahead; a row's chunks are written and read by four lanes of one
-// wave (same-wave LDS order, no barrier needed).
-// Lane l of producer wave w takes rows 16 w + (l & 15) and 64 + 16 w + (l & 15) and
-// 16-byte piece l >> 4 (token slots likewise), so each 16-lane group of a tile store
-// writes 256 contiguous bytes and the stores are free of LDS bank conflicts.
+// so each weight block is regenerated once per pass over its expert's tokens.  It walks
+// K in 64-k steps, one barrier per step.  The waves split by role, two of each role on
+// every SIMD, so that a SIMD's vector ALU and its matrix core work at the same time:
+//   - producers (waves 0-7) regenerate the next step's A tile (two blocks per lane) and
+//     stage its B tile (the step's 128-byte slice of every token row), both in LDS;
+//   - consumers (waves 8-15), wave (row half rh, token quarter tq), multiply their two
+//     32-row A tiles (gate and up rows of one half, or two row tiles) with three
+//     32-token B tiles on v_mfma_f32_32x32x16_bf16 (four k16 slices per step),
+//     accumulators in registers, and write the results.
+// LDS tiles are stored per k16 slice ([slice][row or token][2 blocks][8 bf16]) so every
+// MFMA fragment is one contiguous 1 KB read.  A and B are double-buffered: the producers
+// fill step s+1 while the consumers multiply step s.  A producer stores step s+1's B
+// slice (loaded during step s-1) first, then issues step s+2's B loads, regenerates step
+// s+1's blocks and reads its stream values for step s+2.  Each B load instruction covers
+// whole 128-byte lines: 8 tokens x 8 pieces.
+// The seed / coefficient / code streams of each 32-block group (four steps) are staged
+// in LDS with 16-byte loads, one buffer: a row's chunks are written and read by four
+// lanes of one wave, so same-wave LDS order puts the group's stores after the previous
+// group's last reads and before its own first (no barrier needed).
+// Lane l of producer wave w takes row 16 w + (l & 15) and blocks l >> 4 and 4 + (l >> 4)
+// of each step, so each 16-lane group of an A store writes 256 contiguous bytes.
 // Workgroups are numbered so that every row group of one expert lands on the same XCD
 // (workgroups are dealt to the 8 XCDs round-robin), keeping that expert's token rows in
 // one L2.
@@ -632,14 +633,15 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
     constexpr int RM = AR / NMAT;             // rows per matrix
     constexpr int NTW = 3;                    // 32-token tiles per consumer wave
     constexpr int NC = 4 * NTW * 32;          // token slots per pass (384)
-    constexpr int NBU = NC * 4 / 512;         // B pieces per producer lane and step (3)
+    constexpr int NQ = 4;                     // k16 slices per 64-k step
+    constexpr int NBU = NC * 8 / 512;         // B pieces per producer lane and step (6)
     constexpr int SROW = 40;                  // staged stream row stride in u16 (80 B: the
                                               // 16 rows a lane group reads start in distinct banks)
-    __shared__ u32x4 As[2][2 * AR * 2];
-    __shared__ u32x4 Bs[2][2 * NC * 2];
-    __shared__ uint16_t Ss[2][AR * SROW];
-    __shared__ uint16_t Cs[2][AR * SROW + 8];
-    __shared__ uint8_t Ds[2][AR * 16];
+    __shared__ u32x4 As[2][NQ * AR * 2];
+    __shared__ u32x4 Bs[2][NQ * NC * 2];
+    __shared__ uint16_t Ss[AR * SROW];
+    __shared__ uint16_t Cs[AR * SROW + 8];
+    __shared__ uint8_t Ds[AR * 16];
     __shared__ uint32_t tab[512];
     fill_lfsr_tables(tab);
 
@@ -686,10 +688,10 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
     const int64_t nblk = (int64_t)M * nbpr;
     const int m0 = rg * RM;
     const int ngroups = nbpr / 32;            // K % 256 == 0
-    const int NS = ngroups * 8;
+    const int NS = ngroups * 4;               // 64-k steps
 
     if (producer) {
-        // ---- producer: A row r (matrix dmat, row drow), 16-byte piece dj --------------
+        // ---- producer: A row r (matrix dmat, row drow), blocks dj and 4 + dj ----------
         const int dj = lane >> 4;
         const int r = 16 * wave + (lane & 15);
         const int dmat = r / RM, drow = r % RM;
@@ -699,9 +701,11 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
         }
         const bool drv = m0 + drow < M;
         const int64_t drowb = (int64_t)(drv ? m0 + drow : M - 1) * nbpr;
-        // LDS tile layout [k half][32-row group][block in half][32 rows]: a half-wave's
-        // fragment read is 512 contiguous bytes (no bank conflicts)
+        // LDS tile layout [k16 slice][32-row group][block in slice][32 rows]: a half-wave's
+        // fragment read is 512 contiguous bytes (no bank conflicts).  Block dj of a step
+        // lies in slice dj >> 1, block 4 + dj in slice 2 + (dj >> 1).
         const int a_slot = ((dj >> 1) * AR + (r & ~31)) * 2 + (dj & 1) * 32 + (r & 31);
+        constexpr int A_HI = 2 * AR * 2;      // offset of slices 2, 3
 
         u32x4 sreg_s, sreg_c, sreg_d;
         auto stream_load = [&](int g) {
@@ -710,29 +714,27 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
             if (dj < P) sreg_c = *reinterpret_cast<const u32x4*>(W.coefs + (b0 * P) / 4 + 8 * dj);
             if (dj == 0) sreg_d = *reinterpret_cast<const u32x4*>(W.codes + b0 / 2);
         };
-        auto stream_store = [&](int buf) {
-            *reinterpret_cast<u32x4*>(&Ss[buf][r * SROW + 8 * dj]) = sreg_s;
+        auto stream_store = [&]() {
+            *reinterpret_cast<u32x4*>(&Ss[r * SROW + 8 * dj]) = sreg_s;
             // missing rows get zero coefficients (zero weights); applied here, not at the
             // load, so the load is not waited for early
             if (dj < P)
-                *reinterpret_cast<u32x4*>(&Cs[buf][r * SROW + 8 * dj]) =
+                *reinterpret_cast<u32x4*>(&Cs[r * SROW + 8 * dj]) =
                     drv ? sreg_c : u32x4{0u, 0u, 0u, 0u};
-            if (dj == 0) *reinterpret_cast<u32x4*>(&Ds[buf][r * 16]) = sreg_d;
+            if (dj == 0) *reinterpret_cast<u32x4*>(&Ds[r * 16]) = sreg_d;
         };
         struct Blk { uint32_t seed, cw, code; };
-        auto fetch = [&](int s) {
-            const int buf = (s >> 3) & 1;
-            const int bl = 4 * (s & 7) + dj;      // block within the group
+        auto fetch1 = [&](int bl) {           // block bl (0..31) of the staged group
             Blk k;
-            k.seed = Ss[buf][r * SROW + bl];
+            k.seed = Ss[r * SROW + bl];
             if constexpr (P == 4) {
-                k.cw = Cs[buf][r * SROW + bl];
+                k.cw = Cs[r * SROW + bl];
             } else {
                 const int n = 3 * bl, sh = 4 * (n & 3);
-                const uint16_t* c = &Cs[buf][r * SROW + (n >> 2)];
+                const uint16_t* c = &Cs[r * SROW + (n >> 2)];
                 k.cw = ((uint32_t)c[0] | ((uint32_t)c[1] << 16)) >> sh;
             }
-            k.code = ((uint32_t)Ds[buf][r * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
+            k.code = ((uint32_t)Ds[r * 16 + (bl >> 1)] >> (4 * (bl & 1))) & 0xFu;
             return k;
         };
         auto regen = [&](const Blk& k, u32x4* dst) {
@@ -742,62 +744,67 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
         };
 
         for (int pass = 0; pass < n_e; pass += NC) {
-            // B staging: token slot 16 (wave + 8 u) + (lane & 15), 16-byte piece dj
+            // B staging: instruction u covers token slots 8 (wave + 8 u) .. +7 (lane & 7),
+            // 16-byte piece p = lane >> 3 of each token's 128-byte slice
+            const int p = lane >> 3;
             const uint16_t* brow[NBU];
-            int bslot[NBU];
 #pragma unroll
             for (int u = 0; u < NBU; ++u) {
-                const int ts = 16 * (wave + 8 * u) + (lane & 15);
+                const int ts = 8 * (wave + 8 * u) + (lane & 7);
                 const int i = min(pass + ts, n_e - 1);
                 int64_t src;
                 if constexpr (MODE == MODE_GEMM) src = i;
                 else if constexpr (MODE == MODE_GATEUP) src = list[i] / a.top_k;
                 else src = list[i];
-                brow[u] = a.x + src * a.ldx + 8 * dj;
-                bslot[u] = ((dj >> 1) * NC + (ts & ~31)) * 2 + (dj & 1) * 32 + (ts & 31);
+                brow[u] = a.x + src * a.ldx + 8 * p;
             }
+            // slot of piece p of token ts: slice p >> 1, block p & 1
+            auto bslot = [&](int u) {
+                const int ts = 8 * (wave + 8 * u) + (lane & 7);
+                return ((p >> 1) * NC + (ts & ~31)) * 2 + (p & 1) * 32 + (ts & 31);
+            };
 
-            // prologue: group 0 staged, group 1 in registers; step 0's weights and B slice
-            // in buffer 0, step 1's B slice in flight, step 1's stream values in registers
+            // prologue: group 0 staged and group 1 in registers; step 0's weights and B
+            // slice in buffer 0; step 1's B slice in registers; step 1's stream values read
             stream_load(0);
-            stream_store(0);
+            stream_store();
             if (ngroups > 1) stream_load(1);
-            u32x4 bA[NBU], bB[NBU];           // two register sets, named statically
+            u32x4 breg[NBU];
 #pragma unroll
-            for (int u = 0; u < NBU; ++u) bA[u] = *reinterpret_cast<const u32x4*>(brow[u]);
+            for (int u = 0; u < NBU; ++u) breg[u] = *reinterpret_cast<const u32x4*>(brow[u]);
+            Blk c0 = fetch1(dj), c1 = fetch1(4 + dj);
+            regen(c0, &As[0][a_slot]);
+            regen(c1, &As[0][A_HI + a_slot]);
 #pragma unroll
-            for (int u = 0; u < NBU; ++u) bB[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32);
-            regen(fetch(0), &As[0][a_slot]);
-            Blk nxt = fetch(1);
+            for (int u = 0; u < NBU; ++u) Bs[0][bslot(u)] = breg[u];
 #pragma unroll
-            for (int u = 0; u < NBU; ++u) Bs[0][bslot[u]] = bA[u];
+            for (int u = 0; u < NBU; ++u) breg[u] = *reinterpret_cast<const u32x4*>(brow[u] + 64);
+            Blk n0 = fetch1(8 + dj), n1 = fetch1(12 + dj);
             __syncthreads();
 
-// Producer side of step s: step s+1's weights into buffer s&1^1, then the stream values
-// of step s+2 (staging the next group when s+2 opens it), step s+2's B loads, and step
-// s+1's B slice (BSTORE) into buffer s&1^1.  Indices past the last step are clamped;
-// those writes land in buffers nobody reads.
-#define SEEDMM_WIDE_PRODUCE(S, BNEXT, BSTORE)                                                 \
-    {                                                                                         \
-        const int s_ = (S), nb_ = (s_ & 1) ^ 1;                                               \
-        regen(nxt, &As[nb_][a_slot]);                                                         \
-        if (((s_ + 2) & 7) == 0 && s_ + 2 < NS) {                                             \
-            const int g2 = (s_ + 2) >> 3;                                                     \
-            stream_store(g2 & 1);                                                             \
-            if (g2 + 1 < ngroups) stream_load(g2 + 1);                                        \
-        }                                                                                     \
-        const int sn_ = min(s_ + 2, NS - 1);                                                  \
-        nxt = fetch(sn_);                                                                     \
-        _Pragma("unroll") for (int u = 0; u < NBU; ++u)                                       \
-            BNEXT[u] = *reinterpret_cast<const u32x4*>(brow[u] + 32 * sn_);                   \
-        _Pragma("unroll") for (int u = 0; u < NBU; ++u) Bs[nb_][bslot[u]] = BSTORE[u];        \
-        __syncthreads();                                                                      \
-    }
-            for (int s = 0; s < NS; s += 2) {     // NS is a multiple of 8
-                SEEDMM_WIDE_PRODUCE(s, bA, bB)
-                SEEDMM_WIDE_PRODUCE(s + 1, bB, bA)
+            // step s: step s+1's B slice and weights into buffer s&1^1, step s+2's B loads,
+            // and step s+2's stream values (staging its group first when it opens one).
+            // Indices past the last step are clamped; those writes land in buffers nobody
+            // reads.
+            for (int s = 0; s < NS; ++s) {
+                const int nb = (s & 1) ^ 1;
+#pragma unroll
+                for (int u = 0; u < NBU; ++u) Bs[nb][bslot(u)] = breg[u];
+                const int sn = min(s + 2, NS - 1);
+#pragma unroll
+                for (int u = 0; u < NBU; ++u) breg[u] = *reinterpret_cast<const u32x4*>(brow[u] + 64 * sn);
+                regen(n0, &As[nb][a_slot]);
+                regen(n1, &As[nb][A_HI + a_slot]);
+                if (((s + 2) & 3) == 0 && s + 2 < NS) {
+                    const int g2 = (s + 2) >> 2;
+                    stream_store();           // after the last reads of group g2 - 1
+                    if (g2 + 1 < ngroups) stream_load(g2 + 1);
+                }
+                const int bl = 8 * (sn & 3) + dj;
+                n0 = fetch1(bl);
+                n1 = fetch1(bl + 4);
+                __syncthreads();
             }
-#undef SEEDMM_WIDE_PRODUCE
             __syncthreads();   // LDS buffers are reused by the next pass
         }
     } else {
@@ -820,13 +827,13 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
             for (int s = 0; s < NS; ++s) {
                 const int buf = s & 1;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bf16x8 A0 = __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta0) * 2 + lane]);
-                    const bf16x8 A1 = __builtin_bit_cast(bf16x8, As[buf][(h * AR + 32 * ta1) * 2 + lane]);
+                for (int q = 0; q < NQ; ++q) {
+                    const bf16x8 A0 = __builtin_bit_cast(bf16x8, As[buf][(q * AR + 32 * ta0) * 2 + lane]);
+                    const bf16x8 A1 = __builtin_bit_cast(bf16x8, As[buf][(q * AR + 32 * ta1) * 2 + lane]);
 #pragma unroll
                     for (int t = 0; t < NTW; ++t) {
                         const bf16x8 Bf =
-                            __builtin_bit_cast(bf16x8, Bs[buf][(h * NC + 32 * (tq * NTW + t)) * 2 + lane]);
+                            __builtin_bit_cast(bf16x8, Bs[buf][(q * NC + 32 * (tq * NTW + t)) * 2 + lane]);
                         acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, Bf, acc[0][t], 0, 0, 0);
                         acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, Bf, acc[1][t], 0, 0, 0);
                     }
