@@ -786,14 +786,26 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
             // and step s+2's stream values (staging its group first when it opens one).
             // Indices past the last step are clamped; those writes land in buffers nobody
             // reads.
+            // The producers leave each barrier together; their B loads are spread over
+            // the step (half before each block) so the vector-memory queue drains while
+            // the vector ALU decodes, instead of stalling every producer at once.
             for (int s = 0; s < NS; ++s) {
                 const int nb = (s & 1) ^ 1;
-#pragma unroll
-                for (int u = 0; u < NBU; ++u) Bs[nb][bslot(u)] = breg[u];
                 const int sn = min(s + 2, NS - 1);
 #pragma unroll
-                for (int u = 0; u < NBU; ++u) breg[u] = *reinterpret_cast<const u32x4*>(brow[u] + 64 * sn);
+                for (int u = 0; u < NBU / 2; ++u) {
+                    Bs[nb][bslot(u)] = breg[u];
+                    breg[u] = *reinterpret_cast<const u32x4*>(brow[u] + 64 * sn);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 regen(n0, &As[nb][a_slot]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = NBU / 2; u < NBU; ++u) {
+                    Bs[nb][bslot(u)] = breg[u];
+                    breg[u] = *reinterpret_cast<const u32x4*>(brow[u] + 64 * sn);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 regen(n1, &As[nb][A_HI + a_slot]);
                 if (((s + 2) & 3) == 0 && s + 2 < NS) {
                     const int g2 = (s + 2) >> 2;
@@ -837,6 +849,15 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
                         acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, Bf, acc[0][t], 0, 0, 0);
                         acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, Bf, acc[1][t], 0, 0, 0);
                     }
+                }
+                // per slice: read A0, A1, B0, B1; two MFMAs on B0 while B2 is read; then
+                // the MFMAs on B1 and B2 (one fragment read in flight behind each pair)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 }
                 __syncthreads();
             }
