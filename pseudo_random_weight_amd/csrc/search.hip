@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/seedmm.h"
@@ -84,6 +85,83 @@ __device__ __forceinline__ bool solve_small(double (&a)[4][4], double (&r)[4], d
     return true;
 }
 
+// The candidates of one seed: every code 0..15 from its solution alpha, in the
+// definition's arithmetic, each compared with the best so far on the whole key
+// (err, seed * 16 + code).
+template <int P, bool WEIGHTED>
+__device__ __forceinline__ void try_codes_of(int seed, const double (&alpha)[4], const double (&w)[8],
+                                             const double (&d)[8], double e0, int exp_bias,
+                                             double& best, int& bkey, uint32_t& bnib) {
+#pragma clang fp contract(off)
+    const Window win = lfsr_window((uint32_t)seed);
+    int Ui[8][P];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < P; ++j) Ui[i][j] = (int)state(win, i * P + j + 1) - 32768;
+    // A NaN coefficient comes only from a NaN alpha (alpha * 2^-e is otherwise a
+    // number, and rint and the clamps keep it one), so the path is chosen once.
+    bool anynan = false;
+#pragma unroll
+    for (int j = 0; j < P; ++j) anynan |= alpha[j] != alpha[j];
+    auto codes_loop = [&](auto nanpath) {
+        constexpr bool NANP = decltype(nanpath)::value;
+#pragma unroll 1
+        for (int code = 0; code < 16; ++code) {
+            const int e = code + exp_bias - 15;
+            const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
+            const int key = seed * 16 + code;
+            int c[P];
+            bool zero = true;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                double q = __builtin_rint(alpha[j] * inv);   // half to even
+                if (q < -8.0) q = -8.0;
+                if (q > 7.0) q = 7.0;
+                c[j] = q != q ? (int)0x80000000 : (int)q;
+                zero &= c[j] == 0;
+            }
+            if (zero) {
+                // |alpha_j| / 2^e only shrinks as the code grows, so every larger
+                // code rounds to zero as well, with error e0 and a larger key
+                if (e0 < best || (e0 == best && key < bkey)) {
+                    best = e0;
+                    bkey = key;
+                    bnib = 0;
+                }
+                break;
+            }
+            double err = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                double v;
+                if constexpr (!NANP) {
+                    int vi = 0;
+#pragma unroll
+                    for (int j = 0; j < P; ++j) vi += Ui[i][j] * c[j];
+                    v = (double)vi;
+                } else {
+                    v = 0.0;
+#pragma unroll
+                    for (int j = 0; j < P; ++j) v += (double)Ui[i][j] * (double)c[j];
+                }
+                const double dd = w[i] - sc * v;
+                err += WEIGHTED ? d[i] * (dd * dd) : dd * dd;
+            }
+            if (err < best || (err == best && key < bkey)) {
+                best = err;
+                bkey = key;
+                uint32_t nib = 0;
+#pragma unroll
+                for (int j = 0; j < P; ++j) nib |= ((uint32_t)c[j] & 0xFu) << (4 * j);
+                bnib = nib;
+            }
+        }
+    };
+    if (anynan) codes_loop(std::true_type{});
+    else codes_loop(std::false_type{});
+}
+
 template <int P, bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int64_t ldw,
                                                 const float* __restrict__ colw, int K,
@@ -120,76 +198,8 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
         uint32_t bnib = 0;
 
         // Every code of one seed, from its solution alpha (the definition's arithmetic).
-        // Lanes see seeds in no particular order, so candidates compare on the whole key
-        // (err, seed * 16 + code).
         auto try_codes = [&](int seed, const double (&alpha)[4]) {
-            const Window win = lfsr_window((uint32_t)seed);
-            int Ui[8][P];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < P; ++j) Ui[i][j] = (int)state(win, i * P + j + 1) - 32768;
-            // A NaN coefficient comes only from a NaN alpha (alpha * 2^-e is otherwise a
-            // number, and rint and the clamps keep it one), so the path is chosen once.
-            bool anynan = false;
-#pragma unroll
-            for (int j = 0; j < P; ++j) anynan |= alpha[j] != alpha[j];
-            auto codes_loop = [&](auto nanpath) {
-                constexpr bool NANP = decltype(nanpath)::value;
-#pragma unroll 1
-                for (int code = 0; code < 16; ++code) {
-                    const int e = code + exp_bias - 15;
-                    const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
-                    const int key = seed * 16 + code;
-                    int c[P];
-                    bool zero = true;
-#pragma unroll
-                    for (int j = 0; j < P; ++j) {
-                        double q = __builtin_rint(alpha[j] * inv);   // half to even
-                        if (q < -8.0) q = -8.0;
-                        if (q > 7.0) q = 7.0;
-                        c[j] = q != q ? (int)0x80000000 : (int)q;
-                        zero &= c[j] == 0;
-                    }
-                    if (zero) {
-                        // |alpha_j| / 2^e only shrinks as the code grows, so every larger
-                        // code rounds to zero as well, with error e0 and a larger key
-                        if (e0 < best || (e0 == best && key < bkey)) {
-                            best = e0;
-                            bkey = key;
-                            bnib = 0;
-                        }
-                        break;
-                    }
-                    double err = 0.0;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        double v;
-                        if constexpr (!NANP) {
-                            int vi = 0;
-#pragma unroll
-                            for (int j = 0; j < P; ++j) vi += Ui[i][j] * c[j];
-                            v = (double)vi;
-                        } else {
-                            v = 0.0;
-#pragma unroll
-                            for (int j = 0; j < P; ++j) v += (double)Ui[i][j] * (double)c[j];
-                        }
-                        const double dd = w[i] - sc * v;
-                        err += WEIGHTED ? d[i] * (dd * dd) : dd * dd;
-                    }
-                    if (err < best || (err == best && key < bkey)) {
-                        best = err;
-                        bkey = key;
-                        uint32_t nib = 0;
-#pragma unroll
-                        for (int j = 0; j < P; ++j) nib |= ((uint32_t)c[j] & 0xFu) << (4 * j);
-                        bnib = nib;
-                    }
-                }
-            };
-            if (anynan) codes_loop(std::true_type{});
-            else codes_loop(std::false_type{});
+            try_codes_of<P, WEIGHTED>(seed, alpha, w, d, e0, exp_bias, best, bkey, bnib);
         };
 
         // Seeds whose systems survive the bound below queue up in LDS; each time 64 are
@@ -336,9 +346,427 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
     }
 }
 
+// ----------------------------------------------------------------------------------
+// Unweighted search, one block per lane.  Without importances A = U^T U depends on the
+// seed alone, so its Cholesky factor is computed once per seed into a table, and the
+// least-squares residual R = e0 - r^T A^-1 r of a (block, seed) pair costs P dot
+// products of length 8 and one forward substitution instead of a full elimination.
+// All lanes of a wave (64 consecutive blocks) walk the seeds 1..65535 in the same order,
+// so each seed's table record is a uniform (scalar) load.  A pair whose bound does not
+// already exceed the lane's best error joins the lane's queue in LDS; the exact
+// definition (elimination with partial pivoting, then every code) runs on queued pairs in
+// rounds, one pair per lane and round, when some queue is full and at the end.  A lane
+// evaluates its own seeds in increasing order, so once its best error is exactly 0 no
+// later seed can win (errors are never negative and later keys are larger).
+//
+// Bound: the table's factor L of A gives R~ = e0 - |y|^2, L y = r.  The factorisation and
+// the substitution are backward stable, so R~ misses R by at most ~c P eps kappa(A) e0
+// (c ~ 10); the table flags a seed usable when A is positive definite with
+// trace(A)^P <= 1e7 det(A), which bounds kappa(A) by 1e7.  The margin 1e-6 e0 covers that
+// error more than 20 times over, so a pair with (R~ - 1e-6 e0)(1 - 1e-12) > best cannot
+// reach an error <= best and skipping it changes nothing.  Unflagged seeds always go to
+// the exact path.
+// ----------------------------------------------------------------------------------
+
+// Table record of a seed, in doubles: U (8 x P, row-major), the strictly lower entries
+// of L row by row, 1 / L_jj, and the usable flag; padded to whole 64-byte lines.
+template <int P> struct SeedRecord {
+    static constexpr int kU = 0, kL = 8 * P, kD = kL + P * (P - 1) / 2, kFlag = kD + P;
+    static constexpr int kSize = P == 4 ? 48 : 32;
+    static_assert(kFlag < kSize, "record layout");
+};
+__device__ double g_seed_table4[65536 * SeedRecord<4>::kSize];
+__device__ double g_seed_table3[65536 * SeedRecord<3>::kSize];
+
+template <int P>
+__global__ __launch_bounds__(256) void k_seed_table(double* __restrict__ tab) {
+    using Rec = SeedRecord<P>;
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s > 65535) return;
+    double* rec = tab + (int64_t)s * Rec::kSize;
+    const Window win = lfsr_window((uint32_t)s);
+    double U[8][P];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            U[i][j] = (double)((int)state(win, i * P + j + 1) - 32768);
+            rec[Rec::kU + i * P + j] = U[i][j];
+        }
+    // products of 16-bit integers and their sums (below 2^34) are exact in double
+    double A[P][P];
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            double a = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a += U[i][j] * U[i][k];
+            A[j][k] = a;
+        }
+    double L[P][P];
+    bool pd = true;
+    double det = 1.0, trace = 0.0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        double dj = A[j][j];
+#pragma unroll
+        for (int k = 0; k < j; ++k) dj -= L[j][k] * L[j][k];
+        if (!(dj > 0.0)) {
+            pd = false;
+            dj = 1.0;
+        }
+        L[j][j] = sqrt(dj);
+        det *= dj;
+        trace += A[j][j];
+#pragma unroll
+        for (int i = j + 1; i < P; ++i) {
+            double v = A[i][j];
+#pragma unroll
+            for (int k = 0; k < j; ++k) v -= L[i][k] * L[j][k];
+            L[i][j] = v / L[j][j];
+        }
+    }
+    int o = Rec::kL;
+#pragma unroll
+    for (int i = 1; i < P; ++i)
+#pragma unroll
+        for (int j = 0; j < i; ++j) rec[o++] = L[i][j];
+#pragma unroll
+    for (int j = 0; j < P; ++j) rec[Rec::kD + j] = 1.0 / L[j][j];
+    double tp = 1.0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) tp *= trace;
+    rec[Rec::kFlag] = (pd && tp <= 1e7 * det) ? 1.0 : 0.0;
+#pragma unroll
+    for (int k = Rec::kFlag + 1; k < Rec::kSize; ++k) rec[k] = 0.0;
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ W, int64_t ldw,
+                                                      int K, int exp_bias, int64_t nblk,
+                                                      const double* __restrict__ tab,
+                                                      uint16_t* __restrict__ seeds,
+                                                      uint16_t* __restrict__ coefs,
+                                                      uint8_t* __restrict__ codes,
+                                                      double* __restrict__ errs) {
+#pragma clang fp contract(off)
+    using Rec = SeedRecord<P>;
+    constexpr int QCAP = 128;                 // wave queue ring (two batches)
+    __shared__ double wv[4][8][64];           // per wave: the weights of its 64 blocks
+    __shared__ double e0v[4][64], bestv[4][64];
+    __shared__ unsigned long long mbits[4][64];   // merge: per block, best error bits,
+    __shared__ int mkey[4][64];                   // its key and its nibbles
+    __shared__ uint32_t mnib[4][64];
+    __shared__ uint32_t qe[4][QCAP];          // queued pairs: seed | block lane << 16
+    __shared__ uint32_t res[256][2];          // per block: seed | code << 16, coefficient nibbles
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t b0 = (int64_t)blockIdx.x * 256;
+    const int64_t b = b0 + threadIdx.x;
+    const bool active = b < nblk;
+
+    double w[8];
+    {
+        const int nbpr = K / 8;
+        const int64_t m = active ? b / nbpr : 0;
+        const int kb = active ? (int)(b % nbpr) : 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = active ? (double)W[m * ldw + 8 * kb + i] : 0.0;
+            wv[wave][i][lane] = w[i];
+        }
+    }
+    // error of the all-zero coefficients, summed exactly as the code loop sums it
+    double e0 = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double dd = w[i] - 0.0;
+        e0 += dd * dd;
+    }
+    e0v[wave][lane] = e0;
+    double best = __builtin_inf();            // this lane's block: best candidate so far
+    int bkey = 0x7FFFFFFF;                    // seed * 16 + code
+    uint32_t bnib = 0;
+    bestv[wave][lane] = best;
+
+    // The definition for the pair (block blk of this wave, seed): system, elimination,
+    // then every code.  A code whose error provably exceeds thr (see below) is not
+    // evaluated; the others are, in the definition's arithmetic, and the best of them
+    // (whole key) is returned in (cb, ck, cn).
+    auto exact = [&](int blk, int seed, double thr, double& cb, int& ck, uint32_t& cn) {
+        double wl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wl[i] = wv[wave][i][blk];
+        const double e0l = e0v[wave][blk];
+        const Window win = lfsr_window((uint32_t)seed);
+        int Ui[8][P];
+        double U[8][P];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                Ui[i][j] = (int)state(win, i * P + j + 1) - 32768;
+                U[i][j] = (double)Ui[i][j];
+            }
+        double a[4][4], a0[4][4], r[4], r0[4], alpha[4];   // a0: diagonal of A
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            r[j] = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[j] += U[i][j] * wl[i];
+            r0[j] = r[j];
+            // products of 16-bit integers and their partial sums (below 2^34) are exact
+            // in double, so A_jk and A_kj are the same double
+#pragma unroll
+            for (int kk = j; kk < P; ++kk) {
+                a[j][kk] = 0.0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a[j][kk] += U[i][j] * U[i][kk];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+#pragma unroll
+            for (int kk = 0; kk < j; ++kk) a[j][kk] = a[kk][j];
+        double a2[4][4];                      // 2 A_jk above the diagonal (exact)
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            a0[j][j] = a[j][j];
+#pragma unroll
+            for (int kk = j + 1; kk < P; ++kk) a2[j][kk] = 2.0 * a[j][kk];
+        }
+        double trace = 0.0;
+#pragma unroll
+        for (int j = 0; j < P; ++j) trace += a[j][j];
+        if (!solve_small<P>(a, r, alpha)) return;
+        // Code filter.  For any coefficients c, err(c) = R + d^T A d exactly, with R the
+        // least-squares residual and d = alpha - 2^e c.  From the computed alpha,
+        // Rt = e0 - r . alpha and the computed d^T A d miss R and d^T A d by at most
+        // ~c P eps kappa(A) (e0 + d^T A d) (c ~ 10; elimination with partial pivoting is
+        // backward stable and A is positive definite).  With kappa(A) <= trace^P / |det|
+        // <= 1e7 the margin 1e-6 (e0 + d^T A d) covers that many times over, so a code
+        // whose filtered value exceeds thr has an error above thr and cannot win.
+        double det = 1.0, ra = 0.0, tp = 1.0;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            det *= a[j][j];
+            ra += r0[j] * alpha[j];
+            tp *= trace;
+        }
+        const bool filt = tp <= 1e7 * fabs(det);
+        const double Rt = e0l - ra;
+        bool anynan = false;
+#pragma unroll
+        for (int j = 0; j < P; ++j) anynan |= alpha[j] != alpha[j];
+        if (anynan) {
+            // only a degenerate system gives a NaN; evaluate it plainly
+            double dd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dd[i] = 1.0;
+            try_codes_of<P, false>(seed, alpha, wl, dd, e0l, exp_bias, cb, ck, cn);
+            return;
+        }
+#pragma unroll 1
+        for (int code = 0; code < 16; ++code) {
+            const int e = code + exp_bias - 15;
+            const double sc = __builtin_ldexp(1.0, e), inv = __builtin_ldexp(1.0, -e);
+            const int key = seed * 16 + code;
+            int c[P];
+            bool zero = true;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                double q = __builtin_rint(alpha[j] * inv);   // half to even
+                if (q < -8.0) q = -8.0;
+                if (q > 7.0) q = 7.0;
+                c[j] = (int)q;
+                zero &= c[j] == 0;
+            }
+            if (zero) {
+                // |alpha_j| / 2^e only shrinks as the code grows, so every larger code
+                // rounds to zero as well, with error e0 and a larger key
+                if (e0l < cb || (e0l == cb && key < ck)) {
+                    cb = e0l;
+                    ck = key;
+                    cn = 0;
+                }
+                break;
+            }
+            if (filt) {
+                // d^T A d = sum_j d_j (A_jj d_j + 2 sum_{k>j} A_jk d_k), fused (the
+                // margin covers the rounding)
+                double d[P];
+#pragma unroll
+                for (int j = 0; j < P; ++j) d[j] = __builtin_fma(-sc, (double)c[j], alpha[j]);
+                double qf = 0.0;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    double t = a0[j][j] * d[j];
+#pragma unroll
+                    for (int kk = j + 1; kk < P; ++kk) t = __builtin_fma(a2[j][kk], d[kk], t);
+                    qf = __builtin_fma(d[j], t, qf);
+                }
+                const double lim = thr < cb ? thr : cb;
+                if (((Rt + qf) - 1e-6 * (e0l + qf)) * (1.0 - 1e-12) > lim) continue;
+            }
+            double err = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                int vi = 0;
+#pragma unroll
+                for (int j = 0; j < P; ++j) vi += Ui[i][j] * c[j];
+                const double dd = wl[i] - sc * (double)vi;
+                err += dd * dd;
+            }
+            if (err < cb || (err == cb && key < ck)) {
+                cb = err;
+                ck = key;
+                uint32_t nib = 0;
+#pragma unroll
+                for (int j = 0; j < P; ++j) nib |= ((uint32_t)c[j] & 0xFu) << (4 * j);
+                cn = nib;
+            }
+        }
+    };
+
+    // The queued pairs, n <= 64 of them from the ring head: lane t evaluates pair t; the
+    // candidates then merge into their blocks' bests through LDS, on whole keys.  Errors
+    // are never negative (nor NaN), so their bit patterns order like the values: a
+    // 64-bit minimum over the bits finds each block's smallest error, a 32-bit minimum
+    // the smallest key among the candidates with that error (the owner first clears the
+    // key when the error went down), and that candidate writes its nibbles.  One wave's
+    // LDS operations take effect in program order.
+    int qh = 0, qn = 0;                       // ring head and length (wave-uniform)
+    mbits[wave][lane] = (unsigned long long)__double_as_longlong(best);
+    mkey[wave][lane] = bkey;
+    mnib[wave][lane] = bnib;
+    auto run_batch = [&](int n) {
+        double cb = __builtin_inf();
+        int ck = 0x7FFFFFFF;
+        uint32_t cn = 0;
+        int blk = 0;
+        if (lane < n) {
+            const uint32_t ent = qe[wave][(qh + lane) & (QCAP - 1)];
+            blk = (int)(ent >> 16);
+            exact(blk, (int)(ent & 0xFFFFu), bestv[wave][blk], cb, ck, cn);
+        }
+        const unsigned long long cbits = (unsigned long long)__double_as_longlong(cb);
+        const bool has = lane < n && ck != 0x7FFFFFFF;
+        if (has) __hip_atomic_fetch_min(&mbits[wave][blk], cbits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        const unsigned long long mine = mbits[wave][lane];
+        if (mine != (unsigned long long)__double_as_longlong(best)) mkey[wave][lane] = 0x7FFFFFFF;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        const bool tie = has && mbits[wave][blk] == cbits;
+        if (tie) __hip_atomic_fetch_min(&mkey[wave][blk], ck, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        if (tie && mkey[wave][blk] == ck) mnib[wave][blk] = cn;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        best = __longlong_as_double((long long)mine);
+        bkey = mkey[wave][lane];
+        bnib = mnib[wave][lane];
+        bestv[wave][lane] = best;
+        qh = (qh + n) & (QCAP - 1);
+        qn -= n;
+    };
+
+#pragma unroll 1
+    for (int s = 1; s <= 65535; ++s) {
+        const double* rec = tab + (int64_t)s * Rec::kSize;
+        // bound (fused multiply-adds are fine here: the margin covers any rounding),
+        // computed for every lane and seed without branches so the record's loads issue
+        // together
+        double r[P], y[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            double acc = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = __builtin_fma(rec[Rec::kU + i * P + j], w[i], acc);
+            r[j] = acc;
+        }
+        double q = 0.0;
+        int o = Rec::kL;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            double v = r[j];
+#pragma unroll
+            for (int k = 0; k < j; ++k) v = __builtin_fma(-rec[o + k], y[k], v);
+            o += j;
+            y[j] = v * rec[Rec::kD + j];
+            q = __builtin_fma(y[j], y[j], q);
+        }
+        const double lb = ((e0 - q) - 1e-6 * e0) * (1.0 - 1e-12);
+        const bool prune = (rec[Rec::kFlag] != 0.0) & (e0 > 0.0) & (best < __builtin_inf()) & (lb > best);
+        const bool keep = active & (best != 0.0) & !prune;
+        const uint64_t bal = __ballot(keep);
+        if (keep) {
+            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+            qe[wave][(qh + qn + __popcll(below)) & (QCAP - 1)] = (uint32_t)s | ((uint32_t)lane << 16);
+        }
+        qn += __popcll(bal);
+        if (qn >= 64) run_batch(64);
+    }
+    if (qn > 0) run_batch(qn);
+
+    if (bkey != 0x7FFFFFFF) {
+        res[threadIdx.x][0] = (uint32_t)(bkey >> 4) | ((uint32_t)(bkey & 15) << 16);
+        res[threadIdx.x][1] = bnib;
+        if (errs && active) errs[b] = best;
+    } else {                                  // no seed had a solvable system
+        res[threadIdx.x][0] = 0u;
+        res[threadIdx.x][1] = 0u;
+        if (errs && active) errs[b] = __builtin_inf();
+    }
+    __syncthreads();
+    // the group's streams: its seeds, nb * P nibbles and nb codes (whole words and bytes:
+    // the group starts at a multiple of 256 blocks)
+    const int nb = (int)(nblk - b0 < 256 ? nblk - b0 : 256);
+    const int tid = threadIdx.x;
+    if (tid < nb) seeds[b0 + tid] = (uint16_t)(res[tid][0] & 0xFFFFu);
+    if (tid < (nb * P + 3) / 4) {             // coefficient word tid of the group
+        uint32_t word = 0;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int n = 4 * tid + qq;       // nibble within the group
+            const int blk = n / P, j = n % P;
+            if (blk < nb) word |= ((res[blk][1] >> (4 * j)) & 0xFu) << (4 * qq);
+        }
+        coefs[b0 * P / 4 + tid] = (uint16_t)word;
+    }
+    if (tid < (nb + 1) / 2) {                 // code byte of blocks 2t, 2t+1
+        uint32_t byte = (res[2 * tid][0] >> 16) & 0xFu;
+        if (2 * tid + 1 < nb) byte |= ((res[2 * tid + 1][0] >> 16) & 0xFu) << 4;
+        codes[b0 / 2 + tid] = (uint8_t)byte;
+    }
+}
+
 }  // namespace seedmm
 
 using namespace seedmm;
+
+namespace {
+std::mutex g_table_mu;
+bool g_table_ready[2][64];   // [P == 4][device]
+}  // namespace
+
+// The per-seed table of P on the current device; the first call on a device fills it on
+// `st` and waits for it, so calls on any stream may read it afterwards.
+static int seed_table(int P, hipStream_t st, const double** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SEEDMM_EHIP;
+    void* p = nullptr;
+    const hipError_t e = P == 4 ? hipGetSymbolAddress(&p, HIP_SYMBOL(g_seed_table4))
+                                : hipGetSymbolAddress(&p, HIP_SYMBOL(g_seed_table3));
+    if (e != hipSuccess || !p) return SEEDMM_EHIP;
+    std::lock_guard<std::mutex> lock(g_table_mu);
+    if (!g_table_ready[P == 4][dev]) {
+        if (P == 4) hipLaunchKernelGGL(k_seed_table<4>, dim3(256), dim3(256), 0, st, (double*)p);
+        else hipLaunchKernelGGL(k_seed_table<3>, dim3(256), dim3(256), 0, st, (double*)p);
+        if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return SEEDMM_EHIP;
+        g_table_ready[P == 4][dev] = true;
+    }
+    *out = (const double*)p;
+    return SEEDMM_OK;
+}
 
 extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, int K, int P,
                              int32_t exp_bias, uint16_t* seeds, uint16_t* coefs,
@@ -350,13 +778,18 @@ extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, 
     if (nblk == 0) return SEEDMM_OK;
     if (!W || !seeds || !coefs || !codes) return SEEDMM_EINVAL;
     hipStream_t st = (hipStream_t)hip_stream;
-    const dim3 grid((unsigned)((nblk + 3) / 4));
-    if (P == 4) {
-        if (colw) hipLaunchKernelGGL((k_search<4, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
-        else hipLaunchKernelGGL((k_search<4, false>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+    if (!colw) {
+        // without importances: one block per lane with the per-seed table
+        const double* tab = nullptr;
+        const int rc = seed_table(P, st, &tab);
+        if (rc != SEEDMM_OK) return rc;
+        const dim3 grid((unsigned)((nblk + 255) / 256));
+        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, tab, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, tab, seeds, coefs, codes, err);
     } else {
-        if (colw) hipLaunchKernelGGL((k_search<3, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
-        else hipLaunchKernelGGL((k_search<3, false>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+        const dim3 grid((unsigned)((nblk + 3) / 4));
+        if (P == 4) hipLaunchKernelGGL((k_search<4, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search<3, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
     }
     return hipGetLastError() == hipSuccess ? SEEDMM_OK : SEEDMM_EHIP;
 }

@@ -481,6 +481,23 @@ def test_search_many_blocks_match_oracle(sm, oracle, P, weighted, M):
 
 
 @pytest.mark.parametrize("P", [4, 3])
+def test_search_ragged_groups_match_oracle(sm, oracle, P):
+    """325 blocks without importances: a full group of 256 blocks and a ragged one of 69,
+    whose last coefficient word (P = 3) is part filled, bit for bit against the oracle."""
+    import torch
+    M, K = 5, 520
+    say("search ragged groups", P, M * K // 8)
+    W = _search_case(M, K, f"rag{P}")
+    ref = oracle.search_matrix(W, P, -4, None)
+    got = sm.search(torch.from_numpy(W).cuda(), P, -4)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got["seeds"].cpu().view(torch.int16).numpy().view(np.uint16), ref["seeds"])
+    np.testing.assert_array_equal(got["coefs"].cpu().view(torch.int16).numpy().view(np.uint16), ref["coefs"])
+    np.testing.assert_array_equal(got["codes"].cpu().numpy(), ref["codes"])
+    np.testing.assert_array_equal(got["err"].cpu().numpy().view(np.uint64), ref["err"].view(np.uint64))
+
+
+@pytest.mark.parametrize("P", [4, 3])
 def test_search_recovers_a_seed_coded_matrix(sm, oracle, P):
     """A matrix decoded from random streams is an exact fit: the GPU encoding decodes back
     to it bit for bit (GPU reconstruct) with zero error in every block."""
