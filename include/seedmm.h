@@ -200,7 +200,12 @@ int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int to
  *   read: seeds uint16[M*K/8], coefs uint16[ceil(M*K/8*P/4)], codes uint8[ceil(M*K/16)],
  *   err: float64[M*K/8] squared error of each block (may be NULL).  A block for which
  *   no seed gives a solvable system gets seed 0, zero coefficients and err = +inf.
- *   Compute: about 1.1e8 double operations per block.
+ *   Pairs (block, seed) that provably cannot win are skipped (a least-squares bound
+ *   with a safe margin); the result is the same as evaluating them all.
+ *   Without importances, the first call on a device for a given P fills per-seed tables
+ *   (static device arrays, about 10 MB per P) on hip_stream and waits for that stream,
+ *   so that first call cannot be captured into a graph; later calls only launch.
+ *   Calls on one device may overlap on different streams.
  * Errors: SEEDMM_EINVAL (null pointer, bad size, P not 3/4, exp_bias outside [-100, 100],
  * ldw < K), SEEDMM_EHIP.
  */

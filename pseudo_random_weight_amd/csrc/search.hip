@@ -349,15 +349,18 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
 // ----------------------------------------------------------------------------------
 // Unweighted search, one block per lane.  Without importances A = U^T U depends on the
 // seed alone, so its Cholesky factor is computed once per seed into a table, and the
-// least-squares residual R = e0 - r^T A^-1 r of a (block, seed) pair costs P dot
-// products of length 8 and one forward substitution instead of a full elimination.
-// All lanes of a wave (64 consecutive blocks) walk the seeds 1..65535 in the same order,
-// so each seed's table record is a uniform (scalar) load.  A pair whose bound does not
-// already exceed the lane's best error joins the lane's queue in LDS; the exact
-// definition (elimination with partial pivoting, then every code) runs on queued pairs in
-// rounds, one pair per lane and round, when some queue is full and at the end.  A lane
-// evaluates its own seeds in increasing order, so once its best error is exactly 0 no
-// later seed can win (errors are never negative and later keys are larger).
+// least-squares residual R = e0 - r^T A^-1 r of a (block, seed) pair costs one forward
+// substitution instead of a full elimination.  The seeds are visited along the
+// register's cycle, x_0 = 1, x_{t+1} = the state after x_t: the seed x_t has states
+// s_k = x_{t+k}, so with c_u = sum_i (x_{u+iP} - 32768) w_i its right-hand side is
+// r_j = c_{t+j+1}, and each step along the cycle needs one new c (8 multiply-adds).
+// All lanes of a wave (64 consecutive blocks) walk the cycle together, so each step's
+// table records are uniform (scalar) loads.  A pair whose bound does not already exceed
+// its block's best error joins the wave's queue in LDS; each time 64 pairs are queued,
+// every lane runs the exact definition (elimination with partial pivoting, then every
+// code) on one of them, whatever its block, and the candidates merge into their blocks.
+// Once a block's best error is exactly 0, a seed can only win with a smaller key
+// (errors are never negative), so seeds with seed * 16 above the best key are skipped.
 //
 // Bound: the table's factor L of A gives R~ = e0 - |y|^2, L y = r.  The factorisation and
 // the substitution are backward stable, so R~ misses R by at most ~c P eps kappa(A) e0
@@ -368,31 +371,52 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
 // the exact path.
 // ----------------------------------------------------------------------------------
 
-// Table record of a seed, in doubles: U (8 x P, row-major), the strictly lower entries
-// of L row by row, 1 / L_jj, and the usable flag; padded to whole 64-byte lines.
+constexpr int kCycle = 65535;                 // the register's period
+constexpr int kXLen = kCycle + 64;            // cycle positions stepped (past one period)
+
+// Factor record of the seed at cycle position t, in doubles: the strictly lower entries
+// of L row by row, 1 / L_jj, the usable flag and the seed (its bits in the low word).
 template <int P> struct SeedRecord {
-    static constexpr int kU = 0, kL = 8 * P, kD = kL + P * (P - 1) / 2, kFlag = kD + P;
-    static constexpr int kSize = P == 4 ? 48 : 32;
-    static_assert(kFlag < kSize, "record layout");
+    static constexpr int kL = 0, kD = P * (P - 1) / 2, kFlag = kD + P, kSeed = kFlag + 1;
+    static constexpr int kSize = P == 4 ? 12 : 8;
+    static_assert(kSeed < kSize, "record layout");
 };
-__device__ double g_seed_table4[65536 * SeedRecord<4>::kSize];
-__device__ double g_seed_table3[65536 * SeedRecord<3>::kSize];
+// X record at cycle position u: x_{u+iP} - 32768, i = 0..7 (one 64-byte line).
+constexpr int kXRecs = kCycle + 8;
+__device__ uint32_t g_cycle[kXLen];
+__device__ double g_xrec4[kXRecs * 8], g_xrec3[kXRecs * 8];
+constexpr int kSteps = kCycle + 1;           // steps walked: the cycle, then seed 1 again
+__device__ double g_chol4[kSteps * SeedRecord<4>::kSize], g_chol3[kSteps * SeedRecord<3>::kSize];
+
+// The cycle positions, one thread (32 states per window).
+__global__ void k_cycle(uint32_t* __restrict__ x) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    uint32_t s = 1;
+    for (int t = 0; t < kXLen; t += 32) {
+        const Window win = lfsr_window(s);
+        x[t] = s;
+        for (int k = 1; k < 32 && t + k < kXLen; ++k) x[t + k] = state(win, k);
+        s = state(win, 32);
+    }
+}
 
 template <int P>
-__global__ __launch_bounds__(256) void k_seed_table(double* __restrict__ tab) {
+__global__ __launch_bounds__(256) void k_seed_tables(const uint32_t* __restrict__ x,
+                                                     double* __restrict__ xrec,
+                                                     double* __restrict__ chol) {
     using Rec = SeedRecord<P>;
-    const int s = blockIdx.x * 256 + threadIdx.x;
-    if (s > 65535) return;
-    double* rec = tab + (int64_t)s * Rec::kSize;
-    const Window win = lfsr_window((uint32_t)s);
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t < kXRecs) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xrec[(int64_t)t * 8 + i] = (double)((int)x[t + i * P] - 32768);
+    }
+    if (t >= kSteps) return;
+    double* rec = chol + (int64_t)t * Rec::kSize;
     double U[8][P];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            U[i][j] = (double)((int)state(win, i * P + j + 1) - 32768);
-            rec[Rec::kU + i * P + j] = U[i][j];
-        }
+        for (int j = 0; j < P; ++j) U[i][j] = (double)((int)x[t + i * P + j + 1] - 32768);
     // products of 16-bit integers and their sums (below 2^34) are exact in double
     double A[P][P];
 #pragma unroll
@@ -438,21 +462,23 @@ __global__ __launch_bounds__(256) void k_seed_table(double* __restrict__ tab) {
 #pragma unroll
     for (int j = 0; j < P; ++j) tp *= trace;
     rec[Rec::kFlag] = (pd && tp <= 1e7 * det) ? 1.0 : 0.0;
+    rec[Rec::kSeed] = __longlong_as_double((long long)x[t]);
 #pragma unroll
-    for (int k = Rec::kFlag + 1; k < Rec::kSize; ++k) rec[k] = 0.0;
+    for (int k = Rec::kSeed + 1; k < Rec::kSize; ++k) rec[k] = 0.0;
 }
 
 template <int P>
 __global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ W, int64_t ldw,
                                                       int K, int exp_bias, int64_t nblk,
-                                                      const double* __restrict__ tab,
+                                                      const double* __restrict__ xtab,
+                                                      const double* __restrict__ ctab,
                                                       uint16_t* __restrict__ seeds,
                                                       uint16_t* __restrict__ coefs,
                                                       uint8_t* __restrict__ codes,
                                                       double* __restrict__ errs) {
 #pragma clang fp contract(off)
     using Rec = SeedRecord<P>;
-    constexpr int QCAP = 128;                 // wave queue ring (two batches)
+    constexpr int QCAP = 256;                 // wave queue ring
     __shared__ double wv[4][8][64];           // per wave: the weights of its 64 blocks
     __shared__ double e0v[4][64], bestv[4][64];
     __shared__ unsigned long long mbits[4][64];   // merge: per block, best error bits,
@@ -669,41 +695,68 @@ __global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ 
         qn -= n;
     };
 
-#pragma unroll 1
-    for (int s = 1; s <= 65535; ++s) {
-        const double* rec = tab + (int64_t)s * Rec::kSize;
-        // bound (fused multiply-adds are fine here: the margin covers any rounding),
-        // computed for every lane and seed without branches so the record's loads issue
-        // together
-        double r[P], y[P];
+    // c_{t+1} .. c_{t+P} of the current cycle position t
+    double cw[P];
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            double acc = 0.0;
+    for (int j = 0; j < P; ++j) {
+        double acc = 0.0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc = __builtin_fma(rec[Rec::kU + i * P + j], w[i], acc);
-            r[j] = acc;
-        }
-        double q = 0.0;
+        for (int i = 0; i < 8; ++i) acc = __builtin_fma(xtab[(1 + j) * 8 + i], w[i], acc);
+        cw[j] = acc;
+    }
+    // One step along the cycle from its records: bound, queue, slide the window.
+    auto step = [&](const double* rec, const double* xn) {
+        // bound (fused multiply-adds are fine here: the margin covers any rounding)
+        double y[P], q = 0.0;
         int o = Rec::kL;
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            double v = r[j];
+            double v = cw[j];
 #pragma unroll
             for (int k = 0; k < j; ++k) v = __builtin_fma(-rec[o + k], y[k], v);
             o += j;
             y[j] = v * rec[Rec::kD + j];
             q = __builtin_fma(y[j], y[j], q);
         }
+        const int s = (int)(uint32_t)__double_as_longlong(rec[Rec::kSeed]);
         const double lb = ((e0 - q) - 1e-6 * e0) * (1.0 - 1e-12);
-        const bool prune = (rec[Rec::kFlag] != 0.0) & (e0 > 0.0) & (best < __builtin_inf()) & (lb > best);
-        const bool keep = active & (best != 0.0) & !prune;
+        const bool prune = ((rec[Rec::kFlag] != 0.0) & (e0 > 0.0) & (best < __builtin_inf()) & (lb > best)) |
+                           ((best == 0.0) & (s * 16 > bkey));
+        const bool keep = active & !prune;
         const uint64_t bal = __ballot(keep);
         if (keep) {
             const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
             qe[wave][(qh + qn + __popcll(below)) & (QCAP - 1)] = (uint32_t)s | ((uint32_t)lane << 16);
         }
         qn += __popcll(bal);
-        if (qn >= 64) run_batch(64);
+        // slide the window: c_{t+P+1} in, c_{t+1} out
+        double cn = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cn = __builtin_fma(xn[i], w[i], cn);
+#pragma unroll
+        for (int j = 0; j + 1 < P; ++j) cw[j] = cw[j + 1];
+        cw[P - 1] = cn;
+    };
+    // Two steps per round, their four records read together (one wait per round).  The
+    // last step revisits seed 1; its pairs merge like any other (same candidates).
+#pragma unroll 1
+    for (int t = 0; t < kSteps; t += 2) {
+        double ra[Rec::kSize], rb[Rec::kSize], xa[8], xb[8];
+        const double* pa = ctab + (int64_t)t * Rec::kSize;
+        const double* pxa = xtab + (int64_t)(t + P + 1) * 8;
+#pragma unroll
+        for (int k = 0; k < Rec::kSize; ++k) {
+            ra[k] = pa[k];
+            rb[k] = pa[Rec::kSize + k];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            xa[i] = pxa[i];
+            xb[i] = pxa[8 + i];
+        }
+        step(ra, xa);
+        step(rb, xb);
+        while (qn >= 64) run_batch(64);
     }
     if (qn > 0) run_batch(qn);
 
@@ -745,26 +798,34 @@ using namespace seedmm;
 
 namespace {
 std::mutex g_table_mu;
+bool g_cycle_ready[64];
 bool g_table_ready[2][64];   // [P == 4][device]
 }  // namespace
 
-// The per-seed table of P on the current device; the first call on a device fills it on
-// `st` and waits for it, so calls on any stream may read it afterwards.
-static int seed_table(int P, hipStream_t st, const double** out) {
+// The cycle and the per-seed tables of P on the current device; the first call on a
+// device fills them on `st` and waits, so calls on any stream may read them afterwards.
+static int seed_tables(int P, hipStream_t st, const double** xt, const double** ct) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SEEDMM_EHIP;
-    void* p = nullptr;
-    const hipError_t e = P == 4 ? hipGetSymbolAddress(&p, HIP_SYMBOL(g_seed_table4))
-                                : hipGetSymbolAddress(&p, HIP_SYMBOL(g_seed_table3));
-    if (e != hipSuccess || !p) return SEEDMM_EHIP;
+    void *x = nullptr, *xr = nullptr, *ch = nullptr;
+    if (hipGetSymbolAddress(&x, HIP_SYMBOL(g_cycle)) != hipSuccess || !x) return SEEDMM_EHIP;
+    const hipError_t e1 = P == 4 ? hipGetSymbolAddress(&xr, HIP_SYMBOL(g_xrec4))
+                                 : hipGetSymbolAddress(&xr, HIP_SYMBOL(g_xrec3));
+    const hipError_t e2 = P == 4 ? hipGetSymbolAddress(&ch, HIP_SYMBOL(g_chol4))
+                                 : hipGetSymbolAddress(&ch, HIP_SYMBOL(g_chol3));
+    if (e1 != hipSuccess || e2 != hipSuccess || !xr || !ch) return SEEDMM_EHIP;
     std::lock_guard<std::mutex> lock(g_table_mu);
     if (!g_table_ready[P == 4][dev]) {
-        if (P == 4) hipLaunchKernelGGL(k_seed_table<4>, dim3(256), dim3(256), 0, st, (double*)p);
-        else hipLaunchKernelGGL(k_seed_table<3>, dim3(256), dim3(256), 0, st, (double*)p);
+        if (!g_cycle_ready[dev]) hipLaunchKernelGGL(k_cycle, dim3(1), dim3(64), 0, st, (uint32_t*)x);
+        const dim3 grid((kXRecs + 255) / 256);   // kXRecs >= kSteps
+        if (P == 4) hipLaunchKernelGGL(k_seed_tables<4>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)xr, (double*)ch);
+        else hipLaunchKernelGGL(k_seed_tables<3>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)xr, (double*)ch);
         if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return SEEDMM_EHIP;
+        g_cycle_ready[dev] = true;
         g_table_ready[P == 4][dev] = true;
     }
-    *out = (const double*)p;
+    *xt = (const double*)xr;
+    *ct = (const double*)ch;
     return SEEDMM_OK;
 }
 
@@ -780,12 +841,12 @@ extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, 
     hipStream_t st = (hipStream_t)hip_stream;
     if (!colw) {
         // without importances: one block per lane with the per-seed table
-        const double* tab = nullptr;
-        const int rc = seed_table(P, st, &tab);
+        const double *xt = nullptr, *ct = nullptr;
+        const int rc = seed_tables(P, st, &xt, &ct);
         if (rc != SEEDMM_OK) return rc;
         const dim3 grid((unsigned)((nblk + 255) / 256));
-        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, tab, seeds, coefs, codes, err);
-        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, tab, seeds, coefs, codes, err);
+        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
     } else {
         const dim3 grid((unsigned)((nblk + 3) / 4));
         if (P == 4) hipLaunchKernelGGL((k_search<4, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
