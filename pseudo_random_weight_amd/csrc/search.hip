@@ -355,10 +355,11 @@ __global__ __launch_bounds__(256) void k_search(const float* __restrict__ W, int
 // s_k = x_{t+k}, so with c_u = sum_i (x_{u+iP} - 32768) w_i its right-hand side is
 // r_j = c_{t+j+1}, and each step along the cycle needs one new c (8 multiply-adds).
 // All lanes of a wave (64 consecutive blocks) walk the cycle together, so each step's
-// table records are uniform (scalar) loads.  A pair whose bound does not already exceed
-// its block's best error joins the wave's queue in LDS; each time 64 pairs are queued,
-// every lane runs the exact definition (elimination with partial pivoting, then every
-// code) on one of them, whatever its block, and the candidates merge into their blocks.
+// table records are uniform (scalar) loads; a workgroup is 8 waves (512 blocks).  A pair
+// whose bound does not already exceed its block's best error joins the wave's queue in
+// LDS; each time 64 pairs are queued, every lane runs the exact definition (elimination
+// with partial pivoting, then every code) on one of them, whatever its block, and the
+// candidates merge into their blocks.
 // Once a block's best error is exactly 0, a seed can only win with a smaller key
 // (errors are never negative), so seeds with seed * 16 above the best key are skipped.
 //
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(256) void k_seed_tables(const uint32_t* __restrict_
 }
 
 template <int P>
-__global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ W, int64_t ldw,
                                                       int K, int exp_bias, int64_t nblk,
                                                       const double* __restrict__ xtab,
                                                       const double* __restrict__ ctab,
@@ -479,15 +480,15 @@ __global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ 
 #pragma clang fp contract(off)
     using Rec = SeedRecord<P>;
     constexpr int QCAP = 256;                 // wave queue ring
-    __shared__ double wv[4][8][64];           // per wave: the weights of its 64 blocks
-    __shared__ double e0v[4][64], bestv[4][64];
-    __shared__ unsigned long long mbits[4][64];   // merge: per block, best error bits,
-    __shared__ int mkey[4][64];                   // its key and its nibbles
-    __shared__ uint32_t mnib[4][64];
-    __shared__ uint32_t qe[4][QCAP];          // queued pairs: seed | block lane << 16
-    __shared__ uint32_t res[256][2];          // per block: seed | code << 16, coefficient nibbles
+    __shared__ double wv[8][8][64];           // per wave: the weights of its 64 blocks
+    __shared__ double e0v[8][64], bestv[8][64];
+    __shared__ unsigned long long mbits[8][64];   // merge: per block, best error bits,
+    __shared__ int mkey[8][64];                   // its key and its nibbles
+    __shared__ uint32_t mnib[8][64];
+    __shared__ uint32_t qe[8][QCAP];          // queued pairs: seed | block lane << 16
+    __shared__ uint32_t res[512][2];          // per block: seed | code << 16, coefficient nibbles
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t b0 = (int64_t)blockIdx.x * 256;
+    const int64_t b0 = (int64_t)blockIdx.x * 512;
     const int64_t b = b0 + threadIdx.x;
     const bool active = b < nblk;
 
@@ -757,6 +758,9 @@ __global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ 
         step(ra, xa);
         step(rb, xb);
         while (qn >= 64) run_batch(64);
+        // every 64 steps the group's waves meet, so they read the same table records
+        // at about the same time and one wave's cache misses are the others' hits
+        if ((t & 63) == 0) __syncthreads();
     }
     if (qn > 0) run_batch(qn);
 
@@ -771,8 +775,8 @@ __global__ __launch_bounds__(256) void k_search_lanes(const float* __restrict__ 
     }
     __syncthreads();
     // the group's streams: its seeds, nb * P nibbles and nb codes (whole words and bytes:
-    // the group starts at a multiple of 256 blocks)
-    const int nb = (int)(nblk - b0 < 256 ? nblk - b0 : 256);
+    // the group starts at a multiple of 512 blocks)
+    const int nb = (int)(nblk - b0 < 512 ? nblk - b0 : 512);
     const int tid = threadIdx.x;
     if (tid < nb) seeds[b0 + tid] = (uint16_t)(res[tid][0] & 0xFFFFu);
     if (tid < (nb * P + 3) / 4) {             // coefficient word tid of the group
@@ -844,9 +848,9 @@ extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, 
         const double *xt = nullptr, *ct = nullptr;
         const int rc = seed_tables(P, st, &xt, &ct);
         if (rc != SEEDMM_OK) return rc;
-        const dim3 grid((unsigned)((nblk + 255) / 256));
-        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
-        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(256), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
+        const dim3 grid((unsigned)((nblk + 511) / 512));
+        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
     } else {
         const dim3 grid((unsigned)((nblk + 3) / 4));
         if (P == 4) hipLaunchKernelGGL((k_search<4, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
