@@ -12,9 +12,12 @@
 // seeds per block; barnson.org post, "GPU search == CPU search": no contracted
 // multiply-adds, so the GPU search returns exactly what a CPU search returns.)
 //
-// Every floating-point step is a separately rounded IEEE double operation in the order
-// written above (sums in increasing i, contraction off), so the result is the same, bit
-// for bit, as any CPU evaluation of that definition.  Three exact shortcuts:
+// Every candidate that can win is evaluated with separately rounded IEEE double
+// operations in the order written above (sums in increasing i, contraction off), and
+// candidates compare on the whole key (err, seed * 16 + code), so the result is the same,
+// bit for bit, as any CPU evaluation of that definition.  Fused multiply-adds appear only
+// in the bounds and filters that decide, with safe margins, which pairs and codes cannot
+// win.  Three exact shortcuts:
 //   - alpha / 2^e is computed as alpha * 2^-e (exact for the normal values involved);
 //   - v_i is an integer below 2^21 in magnitude, summed in int32 and converted exactly
 //     (a NaN coefficient, which only a degenerate system could produce, takes the
@@ -22,11 +25,14 @@
 //   - once every coefficient of a seed rounds to zero, all larger codes do too and all
 //     have the same error (that of zero coefficients), so only the first is compared.
 //
-// Mapping: one wave per block; lane l tries seeds 1 + l + 64 k in increasing order and
-// keeps its best candidate with a strict comparison (so ties keep its lower seed, then
-// its lower code); a wave reduction takes the lexicographic minimum.  A 256-thread
-// workgroup owns 4 consecutive blocks, whose coefficient nibbles fill whole words for
-// P = 3 and 4 and whose codes fill whole bytes, so it writes its streams without races.
+// Two kernels:
+//   - k_search (with importances): one wave per block; lane l tries seeds 1 + l + 64 k,
+//     each building and solving its own system, and a wave reduction takes the
+//     lexicographic minimum.  A 256-thread workgroup owns 4 consecutive blocks, whose
+//     coefficient nibbles fill whole words for P = 3 and 4 and whose codes fill whole
+//     bytes, so it writes its streams without races.
+//   - k_search_lanes (without importances): one block per lane, a per-seed table and a
+//     walk along the register's cycle (see there); a workgroup owns 512 blocks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
