@@ -175,7 +175,11 @@ int seedmm_moe_timed(const int32_t *topk_ids, const float *topk_w, int T, int to
  *   experts before e), i.e. the experts' own streams concatenated in expert order.
  *   Requires (I*H/8) % 4 == 0.  Other arguments, results and errors as seedmm_moe
  *   (SEEDMM_EINVAL also for a NULL p4mask).  Each expert kernel runs once per P; a
- *   launch serves only the experts of its P.
+ *   launch serves only the experts of its P.  The P = 3 launches run on a stream the
+ *   library owns (one per device, default priority, created by the first call made
+ *   outside graph capture), forked from hip_stream and joined back into it with events,
+ *   so all work still completes in hip_stream's order and graph capture on hip_stream
+ *   records it; if that stream cannot be created, both launches run on hip_stream.
  */
 int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
                      const void *x, float *y, int E, int H, int I, const uint32_t *p4mask,

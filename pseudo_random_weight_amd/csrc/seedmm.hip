@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/seedmm.h"
 #include "moe_layer.hpp"
 #include "seed_decode.hpp"
@@ -1080,18 +1082,70 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     }
 }
 
+// A second stream per device (default priority) with a fork and a join event, for the
+// two launches of a mixed pack.  Created on first use outside graph capture; null if that
+// fails, and then the launches stay on the caller's stream.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+SideStream* side_stream(hipStream_t st) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream& ss = g_side[dev];
+    if (ss.s) return &ss;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+        if (f) (void)hipEventDestroy(f);
+        (void)hipStreamDestroy(s);
+        return nullptr;
+    }
+    ss.fork = f;
+    ss.join = j;
+    ss.s = s;
+    return &ss;
+}
+
 // P = 3 or 4, or P = 0 for mixed packs (a.p4mask): then one launch per P, each serving
-// only the experts of its own P.
+// only the experts of its own P.  The two write disjoint rows (an expert's pairs belong
+// to one P), so the P = 3 launch runs on the side stream, forked from and joined back
+// into `st` with events (which graph capture records as dependencies): the two grids
+// share the chip instead of each leaving it part empty at its tail.
 template <int MODE>
 void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
-    if (P == 0 || P == 4) {
-        if (vec) launch_mfma<4, true, MODE>(a, prefill, gridy, st);
-        else launch_mfma<4, false, MODE>(a, prefill, gridy, st);
+    auto run = [&](int p, hipStream_t s) {
+        if (p == 4) {
+            if (vec) launch_mfma<4, true, MODE>(a, prefill, gridy, s);
+            else launch_mfma<4, false, MODE>(a, prefill, gridy, s);
+        } else {
+            if (vec) launch_mfma<3, true, MODE>(a, prefill, gridy, s);
+            else launch_mfma<3, false, MODE>(a, prefill, gridy, s);
+        }
+    };
+    if (P != 0) {
+        run(P, st);
+        return;
     }
-    if (P == 0 || P == 3) {
-        if (vec) launch_mfma<3, true, MODE>(a, prefill, gridy, st);
-        else launch_mfma<3, false, MODE>(a, prefill, gridy, st);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = side_stream(st);
+    if (!ss || hipEventRecord(ss->fork, st) != hipSuccess ||
+        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+        run(4, st);
+        run(3, st);
+        return;
     }
+    run(3, ss->s);
+    run(4, st);
+    (void)hipEventRecord(ss->join, ss->s);
+    (void)hipStreamWaitEvent(st, ss->join, 0);
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }

@@ -575,3 +575,44 @@ def test_moe_mixed_with_one_p_is_the_uniform_layer(sm, P, T):
     y_uni, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
     y_mix, _ = _run_mixed(sm, (gate, up, down), [P] * E, ids, w, x, E, H, I)
     assert np.array_equal(y_uni.view(np.uint32), y_mix.view(np.uint32))
+
+
+def test_moe_mixed_graph_replays_match_eager(sm):
+    """The mixed layer (its P = 3 launches forked onto a second stream and joined back)
+    captured in a HIP graph: every replay, with eager work and synchronisations between
+    replays, gives the eager result bit for bit."""
+    import torch
+    E, H, I, k, T = 100, 2048, 1024, 8, 16
+    Ps = [4 if v else 3 for v in (synth.uniform_u64(synth.config_seed(10), "mix.P", E) & np.uint64(1))]
+    say("moe mixed graph replay", sum(p == 4 for p in Ps))
+    mats = _mixed(E, H, I, Ps, "mxr")
+    base = synth.config_seed(10)
+    ids, w = synth.route_topk(base, "mxr.r", T, E, k)
+    x = synth.normal_f32(base, "mxr.x", (T, H))
+    y_ref, _ = _run_mixed(sm, mats, Ps, ids, w, x, E, H, I)
+    g, u, d = (dev(m) for m in mats)
+    mask = sm.p4_mask(Ps, "cuda")
+    ids_t, w_t = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    xt, _ = bf16_tensor(x)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sm.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    call = lambda ids_in, y_out: sm.moe_mixed(ids_in, w_t, xt, E, H, I, mask, g, u, d, Ps=Ps,
+                                              y=y_out, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(ids_t, y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    G = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(G):
+        call(ids_t, y)
+    other = torch.from_numpy(np.roll(ids, 1, axis=0)).cuda()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0xFF)
+        G.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), rep
+        call(other, torch.empty_like(y))
+        torch.cuda.synchronize()
