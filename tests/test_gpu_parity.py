@@ -323,11 +323,12 @@ def test_moe_graph_replays_match_eager(sm):
         torch.cuda.synchronize()
 
 
-def test_moe_prefill_path_small(sm, oracle):
+@pytest.mark.parametrize("P", [4, 3])
+def test_moe_prefill_path_small(sm, oracle, P):
     # >= 64 tokens per expert selects the prefill shape; small dims keep the oracle quick
-    say("moe prefill small")
-    T, E, H, I, P, k = 600, 8, 256, 128, 4, 2
-    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 4, "pfs")
+    say("moe prefill small", P)
+    T, E, H, I, k = 600, 8, 256, 128, 2
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 4, "pfs" if P == 4 else "pfs3")
     y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
     ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
     assert rel_l2(y, ref) <= 1e-2
