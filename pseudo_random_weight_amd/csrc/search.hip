@@ -549,12 +549,13 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
             for (int i = 0; i < 8; ++i) r[j] += U[i][j] * wl[i];
             r0[j] = r[j];
             // products of 16-bit integers and their partial sums (below 2^34) are exact
-            // in double, so A_jk and A_kj are the same double
+            // in double, so A_jk and A_kj are the same double, and a fused multiply-add
+            // gives the same bits as the separate operations
 #pragma unroll
             for (int kk = j; kk < P; ++kk) {
                 a[j][kk] = 0.0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a[j][kk] += U[i][j] * U[i][kk];
+                for (int i = 0; i < 8; ++i) a[j][kk] = __builtin_fma(U[i][j], U[i][kk], a[j][kk]);
             }
         }
 #pragma unroll
