@@ -949,48 +949,92 @@ constexpr int kDispTile = 8192;
 
 __device__ __forceinline__ int disp_slot(int i) { return i + (i >> 5); }
 
+// One tile of pairs [t0, t0 + n): the pairs routed to expert e, written in pair order from
+// list slot `done` on (slots at or past T are dropped: ids repeated within a token).
+// Returns the number of matches in the tile.  Uses s_ids and wsum; ends with a barrier.
+__device__ __forceinline__ int dispatch_tile(const int32_t* __restrict__ ids, int t0, int n, int e,
+                                             int T, int done, int32_t* __restrict__ out,
+                                             int32_t* s_ids, int* wsum) {
+    const int tid = threadIdx.x;
+    {   // all of a thread's loads in flight at once, then the LDS stores
+        int32_t v[kDispTile / 256];
+#pragma unroll
+        for (int k = 0; k < kDispTile / 256; ++k) {
+            const int i = tid + 256 * k;
+            v[k] = i < n ? ids[t0 + i] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kDispTile / 256; ++k) {
+            const int i = tid + 256 * k;
+            if (i < n) s_ids[disp_slot(i)] = v[k];
+        }
+    }
+    __syncthreads();
+    const int R = (n + 255) / 256;
+    const int p0 = min(tid * R, n), p1 = min(p0 + R, n);
+    int c = 0;
+    for (int p = p0; p < p1; ++p) c += s_ids[disp_slot(p)] == e;
+    int tile_total;
+    int slot = done + wg_exclusive_scan(c, wsum, tile_total);
+    if (c > 0) {
+        for (int p = p0; p < p1; ++p) {
+            if (s_ids[disp_slot(p)] == e) {
+                if (slot < T) out[slot] = t0 + p;   // ids repeated within a token: dropped
+                ++slot;
+            }
+        }
+    }
+    __syncthreads();   // the tile and wsum are reused
+    return tile_total;
+}
+
 __global__ __launch_bounds__(256) void k_dispatch(const int32_t* __restrict__ ids, int total,
                                                   int T, int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ lists) {
     __shared__ int32_t s_ids[kDispTile + kDispTile / 32];
     __shared__ int wsum[4];
-    const int e = blockIdx.x, tid = threadIdx.x;
+    const int e = blockIdx.x;
     int32_t* out = lists + (int64_t)e * T;
     int done = 0;   // matches in earlier tiles
-    for (int t0 = 0; t0 < total; t0 += kDispTile) {
-        const int n = min(kDispTile, total - t0);
-        {   // all of a thread's loads in flight at once, then the LDS stores
-            int32_t v[kDispTile / 256];
-#pragma unroll
-            for (int k = 0; k < kDispTile / 256; ++k) {
-                const int i = tid + 256 * k;
-                v[k] = i < n ? ids[t0 + i] : 0;
-            }
-#pragma unroll
-            for (int k = 0; k < kDispTile / 256; ++k) {
-                const int i = tid + 256 * k;
-                if (i < n) s_ids[disp_slot(i)] = v[k];
-            }
-        }
-        __syncthreads();
-        const int R = (n + 255) / 256;
-        const int p0 = min(tid * R, n), p1 = min(p0 + R, n);
-        int c = 0;
-        for (int p = p0; p < p1; ++p) c += s_ids[disp_slot(p)] == e;
-        int tile_total;
-        int slot = done + wg_exclusive_scan(c, wsum, tile_total);
-        if (c > 0) {
-            for (int p = p0; p < p1; ++p) {
-                if (s_ids[disp_slot(p)] == e) {
-                    if (slot < T) out[slot] = t0 + p;   // ids repeated within a token: dropped
-                    ++slot;
-                }
-            }
-        }
-        done += tile_total;
-        __syncthreads();   // the tile and wsum are reused
+    for (int t0 = 0; t0 < total; t0 += kDispTile)
+        done += dispatch_tile(ids, t0, min(kDispTile, total - t0), e, T, done, out, s_ids, wsum);
+    if (threadIdx.x == 0) counts[e] = done < T ? done : T;
+}
+
+// Many pairs: the same lists from two launches over (expert, tile) workgroups, so the
+// tiles of one expert run side by side.  First each workgroup counts its expert's pairs
+// in its tile (cc[tile][e]); then each writes them from the slot that the earlier tiles'
+// counts give, and the last tile writes the expert's count.
+__global__ __launch_bounds__(256) void k_dispatch_count(const int32_t* __restrict__ ids, int total,
+                                                        int E, int32_t* __restrict__ cc) {
+    __shared__ int wsum[4];
+    const int e = blockIdx.x, tile = blockIdx.y, tid = threadIdx.x;
+    const int t0 = tile * kDispTile, n = min(kDispTile, total - t0);
+    int c = 0;
+#pragma unroll 4
+    for (int i = tid; i < n; i += 256) c += ids[t0 + i] == e;
+    int tile_total;
+    (void)wg_exclusive_scan(c, wsum, tile_total);
+    if (tid == 0) cc[(int64_t)tile * E + e] = tile_total;
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restrict__ ids, int total,
+                                                          int T, int E,
+                                                          const int32_t* __restrict__ cc,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ lists) {
+    __shared__ int32_t s_ids[kDispTile + kDispTile / 32];
+    __shared__ int wsum[4];
+    const int e = blockIdx.x, tile = blockIdx.y;
+    int done = 0;
+    for (int t = 0; t < tile; ++t) done += cc[(int64_t)t * E + e];
+    const int t0 = tile * kDispTile;
+    const int got = dispatch_tile(ids, t0, min(kDispTile, total - t0), e, T, done,
+                                  lists + (int64_t)e * T, s_ids, wsum);
+    if (tile == (int)gridDim.y - 1 && threadIdx.x == 0) {
+        const int all = done + got;
+        counts[e] = all < T ? all : T;
     }
-    if (tid == 0) counts[e] = done < T ? done : T;
 }
 
 // y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.
@@ -1151,8 +1195,10 @@ void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct MoeLayout {
-    size_t counts, lists, h, o, total;
+    size_t counts, lists, h, o, cc, total;
 };
+
+int dispatch_tiles(int64_t pairs) { return (int)((pairs + kDispTile - 1) / kDispTile); }
 
 bool moe_layout(int T, int top_k, int E, int H, int I, MoeLayout* L) {
     if (T < 0 || top_k < 1 || E < 1 || H < 0 || I < 0) return false;
@@ -1161,7 +1207,9 @@ bool moe_layout(int T, int top_k, int E, int H, int I, MoeLayout* L) {
     L->lists = L->counts + align_up(sizeof(int32_t) * (size_t)E);
     L->h = L->lists + align_up(sizeof(int32_t) * (size_t)E * (size_t)T);
     L->o = L->h + align_up(sizeof(uint16_t) * pairs * (size_t)I);
-    L->total = L->o + align_up(sizeof(float) * pairs * (size_t)H);
+    L->cc = L->o + align_up(sizeof(float) * pairs * (size_t)H);
+    const int tiles = dispatch_tiles((int64_t)pairs);
+    L->total = L->cc + (tiles > 1 ? align_up(sizeof(int32_t) * (size_t)tiles * (size_t)E) : 0);
     return true;
 }
 
@@ -1299,9 +1347,19 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     // one token: the expert kernels read its top_k ids directly (no dispatch)
     const bool one = T == 1;
     mark(0);
-    if (!one)
-        hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T, counts,
-                           lists);
+    if (!one) {
+        const int tiles = dispatch_tiles((int64_t)T * top_k);
+        if (tiles > 1) {
+            int32_t* cc = (int32_t*)(ws + L.cc);
+            hipLaunchKernelGGL(k_dispatch_count, dim3(E, tiles), dim3(256), 0, st, topk_ids,
+                               T * top_k, E, cc);
+            hipLaunchKernelGGL(k_dispatch_scatter, dim3(E, tiles), dim3(256), 0, st, topk_ids,
+                               T * top_k, T, E, (const int32_t*)cc, counts, lists);
+        } else {
+            hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, st, topk_ids, T * top_k, T,
+                               counts, lists);
+        }
+    }
     mark(1);
 
     const int pairs = T * top_k;

@@ -189,6 +189,32 @@ def test_dispatch_groups_pairs_in_order(sm):
             np.testing.assert_array_equal(lists[e, :counts[e]], np.nonzero(flat == e)[0])
 
 
+def test_layer_dispatch_many_pairs_in_order(sm):
+    """The layer's own dispatch for many pairs (two launches over expert x tile
+    workgroups): the per-expert lists it leaves at the start of its workspace (counts,
+    then the lists from the next 256-byte boundary) hold each expert's pairs in pair
+    order."""
+    import torch
+    E, H, I, P, k = 100, 2048, 1024, 4, 8
+    for T in (1500, 4096):                      # 12,000 and 32,768 pairs: 2 and 4 tiles
+        say("layer dispatch", T)
+        gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2, f"ld{T}")
+        g, u, d = dev(gate), dev(up), dev(down)
+        xt, _ = bf16_tensor(x)
+        ws = torch.empty(sm.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+        sm.moe(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), xt, E, H, I, P, g, u, d,
+               workspace=ws)
+        torch.cuda.synchronize()
+        raw = ws.cpu().numpy()
+        counts = raw[:4 * E].view(np.int32)
+        off = (4 * E + 255) // 256 * 256
+        lists = raw[off:off + 4 * E * T].view(np.int32).reshape(E, T)
+        flat = ids.reshape(-1)
+        np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+        for e in range(E):
+            np.testing.assert_array_equal(lists[e, :counts[e]], np.nonzero(flat == e)[0])
+
+
 _LAYERS = {}
 
 
