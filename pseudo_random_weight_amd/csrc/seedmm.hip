@@ -325,6 +325,8 @@ struct MfmaArgs {
     const int32_t* slot;    // expert cache: int32[E], slot of expert e's streams (null:
                             // stacked experts, expert e at position e)
     int64_t slot_stride;    // expert cache: bytes from one slot to the next
+    int e_lo, e_hi;         // prefill kernel: serve experts e_lo <= e < e_hi only (e_hi = 0:
+                            // all E)
 };
 
 // Pair lists of the one-token path: slot y's list is the single pair index y.
@@ -664,10 +666,11 @@ __global__ __launch_bounds__(1024, 1) void k_wide(const MfmaArgs a) {
     int e = 0, n_e = a.N;
     const int32_t* list = nullptr;
     if constexpr (MODE != MODE_GEMM) {
+        const int ehi = a.e_hi > 0 ? a.e_hi : a.E;
         int found = -1, cum = 0;
-        for (int base = 0; base < a.E && found < 0; base += 64) {
+        for (int base = a.e_lo; base < ehi && found < 0; base += 64) {
             const int idx = base + lane;
-            const bool act = idx < a.E && a.counts[idx] > 0 &&
+            const bool act = idx < ehi && a.counts[idx] > 0 &&
                              (!a.p4mask || p4_of(a.p4mask, idx) == (P == 4));
             const uint64_t bal = __ballot(act);
             const int c = __popcll(bal);
@@ -1192,6 +1195,9 @@ void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, 
     (void)hipStreamWaitEvent(st, ss->join, 0);
 }
 
+// Prefill split point: experts e < E * kSplitNum / kSplitDen on the caller's stream.
+constexpr int kSplitNum = 1, kSplitDen = 2;
+
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct MoeLayout {
@@ -1379,8 +1385,6 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     a.p4mask = p4mask;
     a.slot = slot;
     a.slot_stride = slot_stride;
-    mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
-    mark(2);
 
     MfmaArgs b = {};
     b.A = down;
@@ -1394,8 +1398,44 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     b.p4mask = p4mask;
     b.slot = slot;
     b.slot_stride = slot_stride;
-    mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
-    mark(3);
+
+    // Prefill with one P: the experts below `cut` run their gate/up and down launches on
+    // the caller's stream, the others on the library's side stream (forked and joined with
+    // events, which graph capture records as dependencies).  One launch of the prefill
+    // kernel holds about 16 workgroups per expert at one workgroup per CU, so its last
+    // round leaves most of the chip idle; with two streams the other part's workgroups
+    // fill that tail.  Timed calls (events) keep the single-stream order.
+    const bool wide = prefill && vec && H % 256 == 0 && I % 256 == 0;
+    bool split = false;
+    if (wide && P != 0 && !events && E >= 2) {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream* ss = side_stream(st);
+        if (ss && hipEventRecord(ss->fork, st) == hipSuccess &&
+            hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
+            const int cut = (int)((int64_t)E * kSplitNum / kSplitDen);
+            MfmaArgs pa[2] = {a, a}, pb[2] = {b, b};
+            int gy[2];
+            for (int part = 0; part < 2; ++part) {
+                pa[part].e_lo = pb[part].e_lo = part ? cut : 0;
+                pa[part].e_hi = pb[part].e_hi = part ? E : cut;
+                const int ne = pa[part].e_hi - pa[part].e_lo;
+                gy[part] = pairs < ne ? pairs : ne;
+            }
+            mfma_dispatch<MODE_GATEUP>(P, vec, pa[0], prefill, gy[0], st);
+            mfma_dispatch<MODE_GATEUP>(P, vec, pa[1], prefill, gy[1], ss->s);
+            mfma_dispatch<MODE_DOWN>(P, vec, pb[0], prefill, gy[0], st);
+            mfma_dispatch<MODE_DOWN>(P, vec, pb[1], prefill, gy[1], ss->s);
+            (void)hipEventRecord(ss->join, ss->s);
+            (void)hipStreamWaitEvent(st, ss->join, 0);
+            split = true;
+        }
+    }
+    if (!split) {
+        mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
+        mark(2);
+        mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
+        mark(3);
+    }
 
     if (!direct) {
         const int64_t n4 = (int64_t)T * (H / 4);
