@@ -360,6 +360,18 @@ def test_moe_prefill_path_small(sm, oracle, P):
     assert rel_l2(y, ref) <= 1e-2
 
 
+def _slot_sum(ws, T, k, E, H, I):
+    """y as the combine defines it from the per-slot outputs o (fp32 [T*k][H]) left in the
+    layer's workspace: o[t*k] + o[t*k+1] + ... in slot order, in fp32."""
+    al = lambda v: (v + 255) // 256 * 256
+    off = al(4 * E) + al(4 * E * T) + al(2 * T * k * I)
+    o = ws[off:off + 4 * T * k * H].cpu().numpy().view(np.float32).reshape(T, k, H)
+    y = o[:, 0].copy()
+    for s in range(1, k):
+        y = y + o[:, s]
+    return y
+
+
 def _raw_events(n):
     """n raw hipEvent_t handles (ints) from the HIP runtime, for the timed layer call."""
     import ctypes
@@ -392,6 +404,9 @@ def test_moe_prefill_two_streams(sm, oracle, E, P):
     torch.cuda.synchronize()
     y_two, y_one = y_two.cpu().numpy(), y_one.cpu().numpy()
     assert np.array_equal(y_two.view(np.uint32), y_one.view(np.uint32))
+    # y is the slot-ordered sum of the per-slot outputs (ws still holds the two-stream
+    # call's: the timed call had its own workspace)
+    assert np.array_equal(y_two.view(np.uint32), _slot_sum(ws, T, k, E, H, I).view(np.uint32))
     ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
     assert rel_l2(y_two, ref) <= 1e-2
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
@@ -412,10 +427,18 @@ def test_moe_prefill_two_streams(sm, oracle, E, P):
 def test_moe_prefill_full_size_sampled(sm, oracle):
     # 4096 tokens through the 100-expert top-8 layer; sampled tokens vs the oracle
     say("moe prefill 4096")
+    import torch
     T, E, H, I, P, k = 4096, 100, 2048, 1024, 4, 8
     gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 4, "pf")
-    y, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    xt, x32 = bf16_tensor(x)
+    ws = torch.empty(sm.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    y = sm.moe(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), xt, E, H, I, P,
+               dev(gate), dev(up), dev(down), workspace=ws)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
     assert np.all(np.isfinite(y))
+    # the combine adds every token's slot rows in slot order, bit for bit
+    assert np.array_equal(y.view(np.uint32), _slot_sum(ws, T, k, E, H, I).view(np.uint32))
     for t in (0, 1234, T - 1):
         ref = oracle.moe(ids[t:t + 1], w[t:t + 1], x32[t:t + 1], E, H, I, P, gate, up, down)
         assert rel_l2(y[t], ref[0]) <= 1e-2, t
