@@ -325,8 +325,8 @@ struct MfmaArgs {
     const int32_t* slot;    // expert cache: int32[E], slot of expert e's streams (null:
                             // stacked experts, expert e at position e)
     int64_t slot_stride;    // expert cache: bytes from one slot to the next
-    int e_lo, e_hi;         // prefill kernel: serve experts e_lo <= e < e_hi only (e_hi = 0:
-                            // all E)
+    int e_lo, e_hi;         // routed kernels: serve experts e_lo <= e < e_hi only (e_hi = 0:
+                            // all E; the one-token path ignores them)
 };
 
 // Pair lists of the one-token path: slot y's list is the single pair index y.
@@ -550,10 +550,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (P ==
     } else if constexpr (MODE != MODE_GEMM) {
         // the target-th active expert (of this launch's P when the pack is mixed)
         const int target = blockIdx.y;
+        const int ehi = a.e_hi > 0 ? a.e_hi : a.E;
         int found = -1, cum = 0;
-        for (int base = 0; base < a.E && found < 0; base += 64) {
+        for (int base = a.e_lo; base < ehi && found < 0; base += 64) {
             const int idx = base + lane;
-            const bool act = idx < a.E && a.counts[idx] > 0 &&
+            const bool act = idx < ehi && a.counts[idx] > 0 &&
                              (!a.p4mask || p4_of(a.p4mask, idx) == (P == 4));
             const uint64_t bal = __ballot(act);
             const int c = __popcll(bal);
@@ -1195,7 +1196,8 @@ void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, 
     (void)hipStreamWaitEvent(st, ss->join, 0);
 }
 
-// Prefill split point: experts e < E * kSplitNum / kSplitDen on the caller's stream.
+// Split point of a multi-token call: experts e < E * kSplitNum / kSplitDen on the caller's
+// stream (an even split measured best, decode and prefill).
 constexpr int kSplitNum = 1, kSplitDen = 2;
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1399,15 +1401,15 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     b.slot = slot;
     b.slot_stride = slot_stride;
 
-    // Prefill with one P: the experts below `cut` run their gate/up and down launches on
-    // the caller's stream, the others on the library's side stream (forked and joined with
-    // events, which graph capture records as dependencies).  One launch of the prefill
-    // kernel holds about 16 workgroups per expert at one workgroup per CU, so its last
-    // round leaves most of the chip idle; with two streams the other part's workgroups
-    // fill that tail.  Timed calls (events) keep the single-stream order.
-    const bool wide = prefill && vec && H % 256 == 0 && I % 256 == 0;
+    // Several tokens, one P: the experts below `cut` run their gate/up and down launches
+    // on the caller's stream, the others on the library's side stream (forked and joined
+    // with events, which graph capture records as dependencies).  Each launch ends in a
+    // partly empty last round of workgroups (for the prefill kernel, one workgroup per CU
+    // and ~16 per expert, most of the chip), and down cannot start before gate/up has
+    // drained; with two streams the other half's workgroups fill those gaps.  Timed calls
+    // (events) keep the single-stream order.
     bool split = false;
-    if (wide && P != 0 && !events && E >= 2) {
+    if (!one && P != 0 && !events && E >= 2) {
         std::lock_guard<std::mutex> lock(g_side_mu);
         SideStream* ss = side_stream(st);
         if (ss && hipEventRecord(ss->fork, st) == hipSuccess &&

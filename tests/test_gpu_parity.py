@@ -384,15 +384,16 @@ def _raw_events(n):
     return out
 
 
-@pytest.mark.parametrize("E,P", [(8, 4), (7, 3)])
-def test_moe_prefill_two_streams(sm, oracle, E, P):
-    """Prefill with H and I multiples of 256 runs each part of the experts on its own
-    stream (caller's and side stream).  Its output equals the single-stream order of the
-    timed call bit for bit (every expert served exactly once, whatever the split point),
-    matches the oracle, and graph replays of it reproduce the eager result bit for bit."""
+@pytest.mark.parametrize("E,P,T", [(8, 4, 600), (7, 3, 600), (12, 4, 16), (5, 3, 9)])
+def test_moe_prefill_two_streams(sm, oracle, E, P, T):
+    """A layer call over several tokens with one P runs each half of the experts on its
+    own stream (caller's and side stream), for the prefill kernels (T = 600 here) and the
+    decode ones (T = 16, 9).  Its output equals the single-stream order of the timed call
+    bit for bit (every expert served exactly once, whatever the split point), matches the
+    oracle, and graph replays of it reproduce the eager result bit for bit."""
     import torch
-    T, H, I, k = 600, 256, 256, 2
-    say("moe prefill two streams", E, P)
+    H, I, k = 256, 256, 2
+    say("moe two streams", E, P, T)
     gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 5, f"pf2s{E}")
     g, u, d = dev(gate), dev(up), dev(down)
     ids_t, w_t = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
