@@ -139,6 +139,14 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
  *   the SwiGLU output is rounded to bf16 before the down product; the slots of a token
  *   are summed in slot order, so results are bit-reproducible and a token's output does
  *   not depend on the other tokens of the batch.
+ *   With T > 1 and E > 1 the expert kernels of experts e >= E/2 run on a stream the
+ *   library owns (one per device, default priority, created by the first such call made
+ *   outside graph capture), forked from hip_stream after the dispatch and joined back
+ *   before the combine with events: all work still completes in hip_stream's order and
+ *   graph capture on hip_stream records it.  If that stream cannot be created,
+ *   everything runs on hip_stream.  Calls from several host threads share that stream
+ *   (the library serialises the enqueue) and stay correct, but their halves then queue
+ *   behind one another.  The output bits are the same either way.
  * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], E < 1 or
  * > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
  * SEEDMM_EALIGN (x not 16-byte aligned or H % 8 != 0), SEEDMM_EWORKSPACE, SEEDMM_EHIP.
@@ -156,7 +164,9 @@ int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
  *   batch (T = 1) runs no dispatch kernel (its top_k ids name the experts directly), so
  *   events[0] and events[1] are recorded back to back.
  * `events` may be NULL and any entry may be NULL.  Same arguments, results and errors
- * as seedmm_moe; no event is recorded when the arguments are rejected.
+ * as seedmm_moe; no event is recorded when the arguments are rejected.  When `events`
+ * is not NULL every kernel runs on hip_stream (no side stream), so the recorded stage
+ * times are those of single launches over all experts.
  */
 int seedmm_moe_timed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
                      const void *x, float *y, int E, int H, int I, int P,
