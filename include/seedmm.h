@@ -143,10 +143,12 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
  *   library owns (one per device, default priority, created by the first such call made
  *   outside graph capture), forked from hip_stream after the dispatch and joined back
  *   before the combine with events: all work still completes in hip_stream's order and
- *   graph capture on hip_stream records it.  If that stream cannot be created,
- *   everything runs on hip_stream.  Calls from several host threads share that stream
- *   (the library serialises the enqueue) and stay correct, but their halves then queue
- *   behind one another.  The output bits are the same either way.
+ *   graph capture on hip_stream records it.  If that stream cannot be created, or
+ *   hip_stream belongs to another device than the current one, everything runs on
+ *   hip_stream.  If the join cannot be recorded the call returns SEEDMM_EHIP without
+ *   launching the combine (y is then not valid).  Calls from several host threads share
+ *   that stream (the library serialises the enqueue) and stay correct, but their halves
+ *   then queue behind one another.  The output bits are the same either way.
  * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], E < 1 or
  * > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
  * SEEDMM_EALIGN (x not 16-byte aligned or H % 8 != 0), SEEDMM_EWORKSPACE, SEEDMM_EHIP.

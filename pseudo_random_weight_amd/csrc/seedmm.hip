@@ -1131,8 +1131,10 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
 }
 
 // A second stream per device (default priority) with a fork and a join event, for the
-// two launches of a mixed pack.  Created on first use outside graph capture; null if that
-// fails, and then the launches stay on the caller's stream.
+// two launches of a mixed pack and the two halves of a multi-token call.  Created on
+// first use outside graph capture; null if that fails or if the caller's stream belongs
+// to another device than the current one, and then the launches stay on the caller's
+// stream.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
@@ -1143,6 +1145,10 @@ SideStream g_side[64];
 SideStream* side_stream(hipStream_t st) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (st) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(st, &sd) != hipSuccess || sd != dev) return nullptr;
+    }
     SideStream& ss = g_side[dev];
     if (ss.s) return &ss;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -1167,8 +1173,10 @@ SideStream* side_stream(hipStream_t st) {
 // to one P), so the P = 3 launch runs on the side stream, forked from and joined back
 // into `st` with events (which graph capture records as dependencies): the two grids
 // share the chip instead of each leaving it part empty at its tail.
+// Returns false only when the join back into `st` could not be recorded (the caller's
+// later work would not wait for the side stream's launch).
 template <int MODE>
-void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
+bool mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     auto run = [&](int p, hipStream_t s) {
         if (p == 4) {
             if (vec) launch_mfma<4, true, MODE>(a, prefill, gridy, s);
@@ -1180,7 +1188,7 @@ void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, 
     };
     if (P != 0) {
         run(P, st);
-        return;
+        return true;
     }
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* ss = side_stream(st);
@@ -1188,12 +1196,12 @@ void mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, 
         hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
         run(4, st);
         run(3, st);
-        return;
+        return true;
     }
     run(3, ss->s);
     run(4, st);
-    (void)hipEventRecord(ss->join, ss->s);
-    (void)hipStreamWaitEvent(st, ss->join, 0);
+    return hipEventRecord(ss->join, ss->s) == hipSuccess &&
+           hipStreamWaitEvent(st, ss->join, 0) == hipSuccess;
 }
 
 // Split point of a multi-token call: experts e < E * kSplitNum / kSplitDen on the caller's
@@ -1408,7 +1416,7 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     // and ~16 per expert, most of the chip), and down cannot start before gate/up has
     // drained; with two streams the other half's workgroups fill those gaps.  Timed calls
     // (events) keep the single-stream order.
-    bool split = false;
+    bool split = false, joined = true;
     if (!one && P != 0 && !events && E >= 2) {
         std::lock_guard<std::mutex> lock(g_side_mu);
         SideStream* ss = side_stream(st);
@@ -1427,17 +1435,19 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
             mfma_dispatch<MODE_GATEUP>(P, vec, pa[1], prefill, gy[1], ss->s);
             mfma_dispatch<MODE_DOWN>(P, vec, pb[0], prefill, gy[0], st);
             mfma_dispatch<MODE_DOWN>(P, vec, pb[1], prefill, gy[1], ss->s);
-            (void)hipEventRecord(ss->join, ss->s);
-            (void)hipStreamWaitEvent(st, ss->join, 0);
+            joined = hipEventRecord(ss->join, ss->s) == hipSuccess &&
+                     hipStreamWaitEvent(st, ss->join, 0) == hipSuccess;
             split = true;
         }
     }
     if (!split) {
-        mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
+        joined = mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
         mark(2);
-        mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st);
+        joined = mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st) && joined;
         mark(3);
     }
+    // without the join the combine could read outputs still being written: report it
+    if (!joined) return SEEDMM_EHIP;
 
     if (!direct) {
         const int64_t n4 = (int64_t)T * (H / 4);
