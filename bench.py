@@ -66,18 +66,24 @@ def parse():
 
 
 def host_cpu():
-    """CPU model and the cores this process may use (for the oracle baseline)."""
-    model = None
+    """CPU model and the cores this process may use (for the oracle baseline): the model
+    name, vendor, family / model / stepping and core counts from /proc/cpuinfo."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                k, v = (p.strip() for p in line.split(":", 1))
+                if k in ("model name", "vendor_id", "cpu family", "model", "stepping",
+                         "cpu MHz", "cache size", "cpu cores", "siblings") and k not in info:
+                    info[k] = v
     except OSError:
         pass
-    return {"model": model, "nproc": len(os.sched_getaffinity(0)),
-            "logical_cpus": os.cpu_count()}
+    return {"model": info.get("model name"), "cpuinfo": info,
+            "nproc": len(os.sched_getaffinity(0)), "logical_cpus": os.cpu_count()}
 
 
 def compressed_bytes_per_matrix(P):
@@ -159,12 +165,12 @@ def warm_replays(torch, graphs, seconds=0.03):
 def graph_step(torch, calls, steps):
     """Wall time per step of HIP-graph replays of `calls` (one captured graph per input
     set, cycled), after an untimed warm-up."""
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
         for c in calls:
             c()
-    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.current_stream().wait_stream(warm)
     torch.cuda.synchronize()
     graphs = []
     for c in calls:
@@ -182,11 +188,12 @@ def graph_step(torch, calls, steps):
     return t
 
 
-def config_lines(torch, seedmm, synth, reps, to_dev, P):
+def config_lines(torch, seedmm, synth, reps, to_dev, P, side):
     """One timed figure for each of the other workloads: the single matrix-vector product
     (256 x 512, fp32 x), one SwiGLU expert (2048 -> 768 -> 2048) at 1 and 8 tokens, the
     P = 3 layer at 1 and 16 tokens, and 4096-token prefill through the bench's own layer
-    (`reps`, whose streams have P coefficients per block)."""
+    (`reps`, whose streams have P coefficients per block).  Multi-token layer calls run
+    half their expert launches on the caller's second stream `side`."""
     dev = torch.device("cuda:0")
     out = {}
     # C1: back-to-back launches on the default stream (launch overhead included), on one
@@ -254,7 +261,8 @@ def config_lines(torch, seedmm, synth, reps, to_dev, P):
                                   ).view(torch.bfloat16).to(dev)
             r = l3[g % 3]
             calls.append(lambda i=torch.from_numpy(ids).to(dev), wt=torch.from_numpy(w).to(dev), xg=xg, r=r:
-                         seedmm.moe(i, wt, xg, E, H, I, 3, r["gate"], r["up"], r["down"], y=y4, workspace=ws))
+                         seedmm.moe(i, wt, xg, E, H, I, 3, r["gate"], r["up"], r["down"], y=y4, workspace=ws,
+                                    side=side))
         t = graph_step(torch, calls, 100 if T4 == 1 else 50)
         c4[f"T{T4}_us"] = t * 1e6
         c4[f"T{T4}_weights_per_s"] = np.mean(dist) * 3 * H * I / t
@@ -273,7 +281,8 @@ def config_lines(torch, seedmm, synth, reps, to_dev, P):
                               ).view(torch.bfloat16).to(dev)
         r = reps[g % len(reps)]
         calls.append(lambda i=torch.from_numpy(ids).to(dev), wt=torch.from_numpy(w).to(dev), xg=xg, r=r:
-                     seedmm.moe(i, wt, xg, E, H, I, P, r["gate"], r["up"], r["down"], y=y5, workspace=ws))
+                     seedmm.moe(i, wt, xg, E, H, I, P, r["gate"], r["up"], r["down"], y=y5, workspace=ws,
+                                side=side))
     t = graph_step(torch, calls, 10)
     flops = 2.0 * T5 * TOPK * 3 * H * I
     out[f"C5_prefill_T4096_P{P}"] = {"ms_per_step": t * 1e3, "tok_s": T5 / t,
@@ -282,7 +291,7 @@ def config_lines(torch, seedmm, synth, reps, to_dev, P):
     return out
 
 
-def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, steps=30):
+def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, side, steps=30):
     """The same layer as a mixed pack: a seeded random half of the experts P = 4, the
     rest P = 3 (seedmm_moe_mixed); HIP-graph replays over six input sets and the weight
     replicas, as for the headline step."""
@@ -307,14 +316,14 @@ def mixed_bench(torch, seedmm, synth, dev, T, replicas, to_dev, steps=30):
     def call(g):
         r = reps[g % len(reps)]
         seedmm.moe_mixed(ids_l[g], w_l[g], x_l[g], E, H, I, mask, r["gate"], r["up"], r["down"],
-                         y=y, workspace=ws, Ps=Ps)
+                         y=y, workspace=ws, Ps=Ps, side=side)
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
         for g in range(6):
             call(g)
-    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.current_stream().wait_stream(warm)
     torch.cuda.synchronize()
     graphs = []
     for g in range(6):
@@ -472,6 +481,8 @@ def main():
                 "exp_bias": torch.from_numpy(m["exp_bias"]).to(dev)}
 
     hipev = HipEvents()
+    # the caller-owned second stream and fork / join events of the layer calls
+    side = seedmm.SideStream(dev)
     host = {n: synth.seed_matrix(base, n, *( (I, H) if n != "down" else (H, I) ), P, E)
             for n in ("gate", "up", "down")}
     reps = []
@@ -549,14 +560,14 @@ def main():
         def call(g):
             r = reps[g % nrep]
             seedmm.moe(ids_d[g], w_d[g], x_d[g], E, H, I, P, r["gate"], r["up"], r["down"],
-                       y=y, workspace=ws)
+                       y=y, workspace=ws, side=side)
 
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
+        warm = torch.cuda.Stream()
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):
             for g in range(NB):
                 call(g)
-        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.current_stream().wait_stream(warm)
         torch.cuda.synchronize()
         graphs = []
         for g in range(NB):
@@ -606,18 +617,23 @@ def main():
     gu_weights = distinct.mean() * 2 * w_per_mat
     alg_ops = gu_weights * (2 * P + 1)       # P states + P integer MACs + 1 scale per weight
     traffic = read_traffic("gateup_T%d_P%d" % (T, P))
+    traffic_note = ("calibrated FETCH_SIZE + WRITE_SIZE per launch read from "
+                    "profiles/hbm_traffic.txt (rocprofv3 counter runs of the same kernel "
+                    "sources, not this run)" if traffic is not None else
+                    "no counter summary for the current kernel sources")
     prefill = T * TOPK >= 64 * E          # the library's switch to the LDS-tiled kernel
     if prefill:
         # the tiled kernel's products run on the matrix cores: useful bf16 flops
         flops = 2.0 * T * TOPK * 2 * H * I
         roofline = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": MFMA_PEAK / 1e12,
                     "unit": "TFLOP/s", "frac": flops / t_gu / MFMA_PEAK, "traffic": traffic,
+                    "traffic_source": traffic_note,
                     "kernel": "k_wide<GATEUP> (prefill: fused gate/up + SwiGLU)",
                     "kernel_us": t_gu * 1e6}
     else:
         roofline = {"bound": "alu", "achieved": alg_ops / t_gu, "peak": VALU_PEAK,
                     "unit": "lane-op/s", "frac": alg_ops / t_gu / VALU_PEAK,
-                    "traffic": traffic,
+                    "traffic": traffic, "traffic_source": traffic_note,
                     "kernel": "k_mfma<GATEUP> (fused gate/up + SwiGLU)",
                     "alg_ops_per_weight": 2 * P + 1,
                     "kernel_us": t_gu * 1e6,
@@ -668,12 +684,16 @@ def main():
                               "gate_up_valu_frac": dis.mean() * 2 * w_per_mat * (2 * P + 1)
                               / st[1] / VALU_PEAK}
         out["by_batch"] = sweep
+        if "1" in sweep:
+            # the one-token step: the vector-ALU fraction of its gate/up kernel (event
+            # timing), next to the headline kernel's
+            out["batch1_gate_up_valu_frac"] = sweep["1"]["gate_up_valu_frac"]
 
     if not args.no_configs:
-        out["configs"] = config_lines(torch, seedmm, synth, reps, to_dev, P)
+        out["configs"] = config_lines(torch, seedmm, synth, reps, to_dev, P, side)
 
     if not args.no_mixed:
-        out["mixed"] = mixed_bench(torch, seedmm, synth, dev, T, args.replicas, to_dev)
+        out["mixed"] = mixed_bench(torch, seedmm, synth, dev, T, args.replicas, to_dev, side)
 
     if not args.no_cache:
         out["expert_cache"] = cache_bench(torch, seedmm, synth, host, P)
@@ -687,34 +707,41 @@ def main():
         ids0 = ids_h[s0]
         x0 = synth.bf16_bits_to_f32(x_d[s0].view(torch.int16).cpu().numpy().view(np.uint16))
         w0 = w_d[s0].cpu().numpy()
-        t0 = time.perf_counter()
-        n = 0
-        while n < T and (time.perf_counter() - t0) < args.cpu_seconds:
-            oracle.moe(ids0[n:n + 1], w0[n:n + 1], x0[n:n + 1], E, H, I, P,
-                       host["gate"], host["up"], host["down"])
-            n += 1
-        t_cpu = (time.perf_counter() - t0) / n * T       # the oracle's cost is linear in tokens
-        t_span = time.perf_counter() - t0
         d0 = len(np.unique(ids0))
-        # the same oracle on one thread, over a few tokens
+
+        def oracle_rate(budget_s, reps=5):
+            """Median over `reps` runs of the oracle's time per token, each run a block of
+            consecutive tokens of the step sized from a first token so that all runs
+            together take about budget_s; returns (s per token, tokens per run)."""
+            t0 = time.perf_counter()
+            oracle.moe(ids0[:1], w0[:1], x0[:1], E, H, I, P, host["gate"], host["up"], host["down"])
+            per = time.perf_counter() - t0
+            n = int(max(1, min(T, budget_s / reps / max(per, 1e-9))))
+            times = []
+            for r_ in range(reps):
+                a = (r_ * n) % max(T - n + 1, 1)
+                t0 = time.perf_counter()
+                oracle.moe(ids0[a:a + n], w0[a:a + n], x0[a:a + n], E, H, I, P,
+                           host["gate"], host["up"], host["down"])
+                times.append((time.perf_counter() - t0) / n)
+            return float(np.median(times)), n, [float(v) for v in times]
+
         threads = oracle.num_threads()
+        t_tok, n_tok, runs = oracle_rate(args.cpu_seconds)
+        t_cpu = t_tok * T                      # the oracle's cost is linear in tokens
         oracle.set_num_threads(1)
-        t1 = time.perf_counter()
-        n1 = 0
-        while n1 < T and (time.perf_counter() - t1) < args.cpu_seconds / 3:
-            oracle.moe(ids0[n1:n1 + 1], w0[n1:n1 + 1], x0[n1:n1 + 1], E, H, I, P,
-                       host["gate"], host["up"], host["down"])
-            n1 += 1
-        t_cpu1 = (time.perf_counter() - t1) / n1 * T
+        t_tok1, n_tok1, runs1 = oracle_rate(args.cpu_seconds / 3)
         oracle.set_num_threads(threads)
+        t_cpu1 = t_tok1 * T
         out["cpu_baseline"] = {
             "value": d0 * 3 * w_per_mat / t_cpu, "unit": "weights/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"oracle MoE on the first {n} of the {T} tokens of one step "
-                      f"({t_span:.1f} s), scaled linearly to the step",
-            "tok_s": T / t_cpu,
+            "sample": f"oracle MoE on blocks of {n_tok} consecutive tokens of one {T}-token step, "
+                      f"median of {len(runs)} runs, scaled linearly to the step",
+            "tok_s": T / t_cpu, "s_per_token_runs": runs,
             "single_thread": {"value": d0 * 3 * w_per_mat / t_cpu1, "tok_s": T / t_cpu1,
-                              "sample": f"first {n1} tokens of the same step, one thread"},
+                              "sample": f"blocks of {n_tok1} tokens, one thread, median of "
+                                        f"{len(runs1)} runs"},
             "host": host_cpu()}
     print(json.dumps(out), flush=True)
 

@@ -28,8 +28,11 @@
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller (e.g. PyTorch tensors).
- *     The library allocates no memory and keeps no mutable global state; calls are
- *     reentrant.  Scratch memory for seedmm_moe is passed in by the caller.
+ *     The library allocates no memory and keeps no mutable global state: no streams,
+ *     events or tables of its own.  Scratch memory (the layer's workspace, the encoder's
+ *     table, a second stream and its events) comes from the caller, so calls are
+ *     reentrant and calls from several host threads are independent as long as they do
+ *     not share a workspace, a table being prepared or a seedmm_side.
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL = the
  *     default stream).  Results are valid after the stream is synchronised.
  *   - Arguments are validated before anything is launched; an error returns a negative
@@ -84,7 +87,9 @@ int seedmm_gemv(const uint16_t *seeds, const uint16_t *coefs, const uint8_t *cod
                 int32_t exp_bias, const float *x, float *y, int M, int K, int P);
 
 /*
- * seedmm_gemv_ex -- Y[n] = W X[n] for N activation rows.
+ * seedmm_gemv_ex -- Y[n] = W X[n] for N activation rows: the product of seedmm_gemv for a
+ * batch of rows that share each regenerated block (barnson.org post, "What I changed:
+ * September 2026": the weights are rebuilt inside the product, never stored).
  *   x: row-major [N][ldx] of dtype x_dtype (SEEDMM_F32 or SEEDMM_BF16 raw bits);
  *   y: fp32 row-major [N][ldy], overwritten (ldy >= M).
  *   fp32 x: fp32 products and sums with exact weights.  bf16 x: the block weights are
@@ -99,8 +104,10 @@ int seedmm_gemv_ex(const uint16_t *seeds, const uint16_t *coefs, const uint8_t *
 
 /*
  * seedmm_reconstruct -- write W[M][K] row-major: fp32 (exact) or bf16 (round to nearest
- * even of the exact fp32).  The reference point for bit-exact checks; the products
- * above never materialise W.
+ * even of the exact fp32).  The reference point for bit-exact checks against a scalar C
+ * reference (barnson.org post, "What I changed: September 2026": every GPU path is held
+ * to a plain C function); the products above never materialise W.  A seed of 0 is
+ * decoded like any other (every state is 0, every basis value -32768).
  * Errors: SEEDMM_EINVAL (null pointer, bad size, P, dtype or exp_bias), SEEDMM_EHIP.
  */
 int seedmm_reconstruct(const uint16_t *seeds, const uint16_t *coefs, const uint8_t *codes,
@@ -108,7 +115,9 @@ int seedmm_reconstruct(const uint16_t *seeds, const uint16_t *coefs, const uint8
                        void *hip_stream);
 
 /*
- * seedmm_moe_dispatch -- group the (token, slot) pairs of a routed batch by expert.
+ * seedmm_moe_dispatch -- group the (token, slot) pairs of a routed batch by expert (the
+ * routed experts of a layer, K2-Horizon card "This upload": 100 routed experts per
+ * layer, top-8; each expert's matrices are then read once for all its tokens).
  *   topk_ids: int32[T][top_k], each in [0, E) and distinct within a token.
  *   counts: int32[E] (out) -- number of pairs routed to each expert;
  *   lists:  int32[E][T] (out) -- expert e's pair indices p = t*top_k + slot, in
@@ -120,7 +129,13 @@ int seedmm_reconstruct(const uint16_t *seeds, const uint16_t *coefs, const uint8
 int seedmm_moe_dispatch(const int32_t *topk_ids, int T, int top_k, int E, int32_t *counts,
                         int32_t *lists, void *hip_stream);
 
-/* Bytes of scratch memory seedmm_moe needs for a batch of T tokens (0 on bad args). */
+/* Bytes of scratch memory seedmm_moe (and _ex, _timed, _mixed, seedmm_cache_moe) needs
+ * for a batch of T tokens routed to top_k of E experts of hidden size H and intermediate
+ * size I (0 on bad args): expert counts int32[E], pair lists int32[E][T], the SwiGLU rows
+ * bf16 [T*top_k][I] and the per-slot outputs fp32 [T*top_k][H], each 256-byte aligned,
+ * plus per-tile counts int32[ceil(T*top_k/8192)][E] above 8,192 pairs.  H and I enter
+ * because the SwiGLU rows and the per-slot outputs dominate the size.  (Routed layer of
+ * the K2-Horizon card, "This upload".) */
 size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
 
 /*
@@ -128,6 +143,8 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
  * are seeds (K2-Horizon card "This upload": routed FFN experts are SeedLM P=4):
  *     y[t] = sum_{s < top_k} topk_w[t][s] * down_e( silu(gate_e x[t]) * (up_e x[t]) ),
  *     e = topk_ids[t][s],  silu(z) = z / (1 + exp(-z)).
+ *   (The pages do not spell out the expert FFN; SwiGLU experts with softmax-weighted
+ *   top-k slots are this library's reading.)
  *   x: bf16 [T][H] (raw bits), y: fp32 [T][H] (overwritten);
  *   gate, up: E stacked [I][H] matrices; down: E stacked [H][I] matrices;
  *   topk_ids: int32[T][top_k], each in [0, E) and distinct within a token (the caller
@@ -136,19 +153,11 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
  *   bytes, 16-byte aligned; its contents need not be initialised.  Calls that overlap
  *   in time must use different workspaces.
  *   Expert products run on the matrix cores with bf16 weights and fp32 accumulation;
- *   the SwiGLU output is rounded to bf16 before the down product; the slots of a token
- *   are summed in slot order, so results are bit-reproducible and a token's output does
- *   not depend on the other tokens of the batch.
- *   With T > 1 and E > 1 the expert kernels of experts e >= E/2 run on a stream the
- *   library owns (one per device, default priority, created by the first such call made
- *   outside graph capture), forked from hip_stream after the dispatch and joined back
- *   before the combine with events: all work still completes in hip_stream's order and
- *   graph capture on hip_stream records it.  If that stream cannot be created, or
- *   hip_stream belongs to another device than the current one, everything runs on
- *   hip_stream.  If the join cannot be recorded the call returns SEEDMM_EHIP without
- *   launching the combine (y is then not valid).  Calls from several host threads share
- *   that stream (the library serialises the enqueue) and stay correct, but their halves
- *   then queue behind one another.  The output bits are the same either way.
+ *   the SwiGLU output h is rounded to bf16 (nearest even) before the down product, in
+ *   the decode and the prefill kernels alike; the slots of a token are summed in slot
+ *   order, so results are bit-reproducible and a token's output does not depend on the
+ *   other tokens of the batch.  All work runs on hip_stream (seedmm_moe_ex splits it
+ *   over a second stream of the caller's).
  * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], E < 1 or
  * > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
  * SEEDMM_EALIGN (x not 16-byte aligned or H % 8 != 0), SEEDMM_EWORKSPACE, SEEDMM_EHIP.
@@ -159,8 +168,42 @@ int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
                void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * seedmm_moe_ex -- the routed layer of seedmm_moe (one P) or seedmm_moe_mixed (P = 0 and
+ * p4mask), with a second stream from the caller.  The layer runs as two independent
+ * halves: for one P, the experts e < E/2 on hip_stream and the others on side->stream;
+ * for mixed packs, the P = 4 launches on hip_stream and the P = 3 launches on
+ * side->stream.  side->fork is recorded on hip_stream after the dispatch and waited for
+ * by side->stream; side->join is recorded on side->stream after its launches and waited
+ * for by hip_stream before the combine.  So all the work still completes in hip_stream's
+ * order, and graph capture on hip_stream records the fork and the join as dependencies.
+ * The two halves' workgroups fill each other's partly empty last rounds (each expert
+ * kernel leaves part of the chip idle at its tail).  The output bits equal seedmm_moe's.
+ *   side: NULL or side->stream NULL = everything on hip_stream.  Otherwise side->stream
+ *   is a stream of hip_stream's device other than hip_stream, and side->fork and
+ *   side->join are events (hipEventDisableTiming is enough), all created and owned by
+ *   the caller.  Calls that may overlap in time must not share a seedmm_side.  One-token
+ *   batches run on hip_stream alone (their kernels fill one wave round).
+ * Errors: as seedmm_moe; SEEDMM_EINVAL also for P = 0 without p4mask, a p4mask with
+ * P = 3 or 4, or a side stream given without both events or equal to hip_stream.  If the
+ * fork cannot be recorded the call runs on hip_stream alone; if the join cannot be
+ * recorded it returns SEEDMM_EHIP without launching the combine (y is then not valid).
+ */
+typedef struct seedmm_side {
+    void *stream;   /* hipStream_t */
+    void *fork;     /* hipEvent_t  */
+    void *join;     /* hipEvent_t  */
+} seedmm_side;
+
+int seedmm_moe_ex(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                  const void *x, float *y, int E, int H, int I, int P, const uint32_t *p4mask,
+                  seedmm_mat gate, seedmm_mat up, seedmm_mat down,
+                  void *workspace, size_t workspace_bytes, void *hip_stream,
+                  const seedmm_side *side);
+
+/*
  * seedmm_moe_timed -- seedmm_moe that also records caller-created hipEvent_t handles on
- * hip_stream between its kernels, for measuring each stage in place:
+ * hip_stream between its kernels, for measuring each stage in place (the pages time
+ * their engines stage by stage: NanoSeedLM documentation index, "Results"):
  *   events[0] before the dispatch, events[1] after it, events[2] after the gate/up
  *   kernel, events[3] after the down kernel, events[4] after the combine.  A one-token
  *   batch (T = 1) runs no dispatch kernel (its top_k ids name the experts directly), so
@@ -187,11 +230,8 @@ int seedmm_moe_timed(const int32_t *topk_ids, const float *topk_w, int T, int to
  *   experts before e), i.e. the experts' own streams concatenated in expert order.
  *   Requires (I*H/8) % 4 == 0.  Other arguments, results and errors as seedmm_moe
  *   (SEEDMM_EINVAL also for a NULL p4mask).  Each expert kernel runs once per P; a
- *   launch serves only the experts of its P.  The P = 3 launches run on a stream the
- *   library owns (one per device, default priority, created by the first call made
- *   outside graph capture), forked from hip_stream and joined back into it with events,
- *   so all work still completes in hip_stream's order and graph capture on hip_stream
- *   records it; if that stream cannot be created, both launches run on hip_stream.
+ *   launch serves only the experts of its P.  All work runs on hip_stream
+ *   (seedmm_moe_ex with P = 0 runs the P = 3 launches on a second stream).
  */
 int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
                      const void *x, float *y, int E, int H, int I, const uint32_t *p4mask,
@@ -218,16 +258,33 @@ int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int to
  *   no seed gives a solvable system gets seed 0, zero coefficients and err = +inf.
  *   Pairs (block, seed) that provably cannot win are skipped (a least-squares bound
  *   with a safe margin); the result is the same as evaluating them all.
- *   Without importances, the first call on a device for a given P fills per-seed tables
- *   (static device arrays, about 10 MB per P) on hip_stream and waits for that stream,
- *   so that first call cannot be captured into a graph; later calls only launch.
- *   Calls on one device may overlap on different streams.
- * Errors: SEEDMM_EINVAL (null pointer, bad size, P not 3/4, exp_bias outside [-100, 100],
- * ldw < K), SEEDMM_EHIP.
+ *   table: without importances (colw NULL), device memory of at least
+ *   seedmm_search_table_bytes(P) bytes, 256-byte aligned, filled for this P by
+ *   seedmm_search_prepare on hip_stream or before it in stream order (a table filled for
+ *   the other P, or not filled, gives undefined results); with importances it is not
+ *   read and may be NULL.  The call only launches kernels (no host wait), so it can be
+ *   captured into a graph.  Calls may share a prepared table and overlap on different
+ *   streams.
+ * Errors: SEEDMM_EINVAL (null pointer, a NULL table without importances, bad size, P not
+ * 3/4, exp_bias outside [-100, 100], ldw < K), SEEDMM_EALIGN (table not 256-byte
+ * aligned), SEEDMM_EHIP.
  */
 int seedmm_search(const float *W, int ldw, const float *colw, int M, int K, int P,
                   int32_t exp_bias, uint16_t *seeds, uint16_t *coefs, uint8_t *codes,
-                  double *err, void *hip_stream);
+                  double *err, const void *table, void *hip_stream);
+
+/*
+ * The encoder's per-seed table for one P (barnson.org post, "LFSR is free": the pages'
+ * encoder and decoder precompute per-seed streams; here the search precomputes, once per
+ * P, each seed's basis rows along the register's cycle and the Cholesky factor of its
+ * normal matrix): about 10.7 MB (P = 4) or 8.7 MB (P = 3) of caller-owned device memory.
+ * seedmm_search_table_bytes returns the size (0 for P not 3/4).  seedmm_search_prepare
+ * fills `table` on hip_stream with kernels only (no host wait; capturable).
+ * Errors: SEEDMM_EINVAL (P not 3/4, NULL table, table_bytes too small), SEEDMM_EALIGN
+ * (table not 256-byte aligned), SEEDMM_EHIP.
+ */
+size_t seedmm_search_table_bytes(int P);
+int seedmm_search_prepare(int P, void *table, size_t table_bytes, void *hip_stream);
 
 /*
  * Expert cache: routed experts resident in host memory, the recently used ones in device
@@ -305,10 +362,12 @@ int seedmm_cache_moe(seedmm_cache *cache, const int32_t *topk_ids_host,
  * host-to-device. */
 int seedmm_cache_stats(const seedmm_cache *cache, uint64_t out[5]);
 
-/* Static description of a status code. */
+/* Static description of a status code (the C engine's error convention: a plain C99
+ * interface, NanoSeedLM README "How it works"). */
 const char *seedmm_strerror(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor); 200 = caller-owned side streams and
+ * encoder tables. */
 int seedmm_version(void);
 
 #ifdef __cplusplus

@@ -43,15 +43,5 @@ def build(verbose: bool = False) -> str:
     return SO
 
 
-def asm(source: str = "seedmm.hip", out: str = None) -> str:
-    """Device assembly of one source file (for inspecting the generated gfx950 code)."""
-    out = out or os.path.join(ROOT, "_work", os.path.splitext(source)[0] + ".s")
-    os.makedirs(os.path.dirname(out), exist_ok=True)
-    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-S",
-           "--cuda-device-only", os.path.join(CSRC, source), "-o", out]
-    subprocess.check_call(cmd)
-    return out
-
-
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -295,7 +295,7 @@ int seedmm_cache_moe(seedmm_cache* c, const int32_t* ids_host, const int32_t* to
     st = seedmm_layer::moe_run(topk_ids, topk_w, T, top_k, x, y, c->E, c->H, c->I, c->P,
                                nullptr, c->slot0[0], c->slot0[1], c->slot0[2], workspace,
                                workspace_bytes, hip_stream, nullptr, c->slot_map_dev,
-                               (int64_t)c->record);
+                               (int64_t)c->record, nullptr);
     if (st == SEEDMM_EHIP) return fail();
     return st;
 }

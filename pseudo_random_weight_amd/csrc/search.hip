@@ -32,11 +32,11 @@
 //     coefficient nibbles fill whole words for P = 3 and 4 and whose codes fill whole
 //     bytes, so it writes its streams without races.
 //   - k_search_lanes (without importances): one block per lane, a per-seed table and a
-//     walk along the register's cycle (see there); a workgroup owns 512 blocks.
+//     walk along the register's cycle (see there); a workgroup owns 512 blocks.  The
+//     table lives in caller-owned device memory, filled by seedmm_search_prepare.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
 #include <type_traits>
 
 #include "../../include/seedmm.h"
@@ -390,10 +390,24 @@ template <int P> struct SeedRecord {
 };
 // X record at cycle position u: x_{u+iP} - 32768, i = 0..7 (one 64-byte line).
 constexpr int kXRecs = kCycle + 8;
-__device__ uint32_t g_cycle[kXLen];
-__device__ double g_xrec4[kXRecs * 8], g_xrec3[kXRecs * 8];
 constexpr int kSteps = kCycle + 1;           // steps walked: the cycle, then seed 1 again
-__device__ double g_chol4[kSteps * SeedRecord<4>::kSize], g_chol3[kSteps * SeedRecord<3>::kSize];
+
+// Layout of the caller's table memory for one P: the cycle positions (uint32[kXLen]),
+// the X records (double[kXRecs][8]) and the factor records (double[kSteps][kSize]),
+// each part starting on a 256-byte boundary.
+struct TableLayout {
+    size_t cycle, xrec, chol, total;
+};
+inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline TableLayout table_layout(int P) {
+    TableLayout L;
+    L.cycle = 0;
+    L.xrec = al256(sizeof(uint32_t) * kXLen);
+    L.chol = L.xrec + al256(sizeof(double) * 8 * (size_t)kXRecs);
+    const int ks = P == 4 ? SeedRecord<4>::kSize : SeedRecord<3>::kSize;
+    L.total = L.chol + al256(sizeof(double) * (size_t)ks * kSteps);
+    return L;
+}
 
 // The cycle positions, one thread (32 states per window).
 __global__ void k_cycle(uint32_t* __restrict__ x) {
@@ -807,42 +821,30 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
 
 using namespace seedmm;
 
-namespace {
-std::mutex g_table_mu;
-bool g_cycle_ready[64];
-bool g_table_ready[2][64];   // [P == 4][device]
-}  // namespace
+extern "C" size_t seedmm_search_table_bytes(int P) {
+    if (P != 3 && P != 4) return 0;
+    return table_layout(P).total;
+}
 
-// The cycle and the per-seed tables of P on the current device; the first call on a
-// device fills them on `st` and waits, so calls on any stream may read them afterwards.
-static int seed_tables(int P, hipStream_t st, const double** xt, const double** ct) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SEEDMM_EHIP;
-    void *x = nullptr, *xr = nullptr, *ch = nullptr;
-    if (hipGetSymbolAddress(&x, HIP_SYMBOL(g_cycle)) != hipSuccess || !x) return SEEDMM_EHIP;
-    const hipError_t e1 = P == 4 ? hipGetSymbolAddress(&xr, HIP_SYMBOL(g_xrec4))
-                                 : hipGetSymbolAddress(&xr, HIP_SYMBOL(g_xrec3));
-    const hipError_t e2 = P == 4 ? hipGetSymbolAddress(&ch, HIP_SYMBOL(g_chol4))
-                                 : hipGetSymbolAddress(&ch, HIP_SYMBOL(g_chol3));
-    if (e1 != hipSuccess || e2 != hipSuccess || !xr || !ch) return SEEDMM_EHIP;
-    std::lock_guard<std::mutex> lock(g_table_mu);
-    if (!g_table_ready[P == 4][dev]) {
-        if (!g_cycle_ready[dev]) hipLaunchKernelGGL(k_cycle, dim3(1), dim3(64), 0, st, (uint32_t*)x);
-        const dim3 grid((kXRecs + 255) / 256);   // kXRecs >= kSteps
-        if (P == 4) hipLaunchKernelGGL(k_seed_tables<4>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)xr, (double*)ch);
-        else hipLaunchKernelGGL(k_seed_tables<3>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)xr, (double*)ch);
-        if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return SEEDMM_EHIP;
-        g_cycle_ready[dev] = true;
-        g_table_ready[P == 4][dev] = true;
-    }
-    *xt = (const double*)xr;
-    *ct = (const double*)ch;
-    return SEEDMM_OK;
+extern "C" int seedmm_search_prepare(int P, void* table, size_t table_bytes, void* hip_stream) {
+    if ((P != 3 && P != 4) || !table) return SEEDMM_EINVAL;
+    const TableLayout L = table_layout(P);
+    if (table_bytes < L.total) return SEEDMM_EINVAL;
+    if (((uintptr_t)table & 255u) != 0) return SEEDMM_EALIGN;
+    hipStream_t st = (hipStream_t)hip_stream;
+    char* base = (char*)table;
+    uint32_t* x = (uint32_t*)(base + L.cycle);
+    hipLaunchKernelGGL(k_cycle, dim3(1), dim3(64), 0, st, x);
+    const dim3 grid((kXRecs + 255) / 256);   // kXRecs >= kSteps
+    if (P == 4) hipLaunchKernelGGL(k_seed_tables<4>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)(base + L.xrec), (double*)(base + L.chol));
+    else hipLaunchKernelGGL(k_seed_tables<3>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)(base + L.xrec), (double*)(base + L.chol));
+    return hipGetLastError() == hipSuccess ? SEEDMM_OK : SEEDMM_EHIP;
 }
 
 extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, int K, int P,
                              int32_t exp_bias, uint16_t* seeds, uint16_t* coefs,
-                             uint8_t* codes, double* err, void* hip_stream) {
+                             uint8_t* codes, double* err, const void* table,
+                             void* hip_stream) {
     if (M < 0 || K < 0 || K % 8 != 0 || (P != 3 && P != 4)) return SEEDMM_EINVAL;
     if (exp_bias < -100 || exp_bias > 100) return SEEDMM_EINVAL;
     if (ldw < K) return SEEDMM_EINVAL;
@@ -852,9 +854,11 @@ extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, 
     hipStream_t st = (hipStream_t)hip_stream;
     if (!colw) {
         // without importances: one block per lane with the per-seed table
-        const double *xt = nullptr, *ct = nullptr;
-        const int rc = seed_tables(P, st, &xt, &ct);
-        if (rc != SEEDMM_OK) return rc;
+        if (!table) return SEEDMM_EINVAL;
+        if (((uintptr_t)table & 255u) != 0) return SEEDMM_EALIGN;
+        const TableLayout L = table_layout(P);
+        const double* xt = (const double*)((const char*)table + L.xrec);
+        const double* ct = (const double*)((const char*)table + L.chol);
         const dim3 grid((unsigned)((nblk + 511) / 512));
         if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
         else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);

@@ -17,8 +17,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
-
 #include "../../include/seedmm.h"
 #include "moe_layer.hpp"
 #include "seed_decode.hpp"
@@ -1041,6 +1039,14 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restr
     }
 }
 
+// y[n][0..M) = 0 for the N rows of a strided fp32 matrix (nm = N * M elements).
+__global__ __launch_bounds__(256) void k_zero_rows(float* __restrict__ y, int ldy, int M,
+                                                   int64_t nm) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nm) return;
+    y[(i / M) * ldy + i % M] = 0.0f;
+}
+
 // y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, int top_k,
                                                  float* __restrict__ y, int H, int T) {
@@ -1130,53 +1136,31 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     }
 }
 
-// A second stream per device (default priority) with a fork and a join event, for the
-// two launches of a mixed pack and the two halves of a multi-token call.  Created on
-// first use outside graph capture; null if that fails or if the caller's stream belongs
-// to another device than the current one, and then the launches stay on the caller's
-// stream.
-struct SideStream {
+// The caller's second stream and its fork / join events (seedmm_side), or all null.
+struct Side {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
+    bool on() const { return s != nullptr; }
+    // hip_stream's work so far becomes a dependency of the side stream's next launches
+    bool fork_from(hipStream_t st) const {
+        return hipEventRecord(fork, st) == hipSuccess && hipStreamWaitEvent(s, fork, 0) == hipSuccess;
+    }
+    // hip_stream's later work waits for everything launched on the side stream
+    bool join_into(hipStream_t st) const {
+        return hipEventRecord(join, s) == hipSuccess && hipStreamWaitEvent(st, join, 0) == hipSuccess;
+    }
 };
-std::mutex g_side_mu;
-SideStream g_side[64];
-
-SideStream* side_stream(hipStream_t st) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    if (st) {
-        hipDevice_t sd = -1;
-        if (hipStreamGetDevice(st, &sd) != hipSuccess || sd != dev) return nullptr;
-    }
-    SideStream& ss = g_side[dev];
-    if (ss.s) return &ss;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    hipStream_t s = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
-        if (f) (void)hipEventDestroy(f);
-        (void)hipStreamDestroy(s);
-        return nullptr;
-    }
-    ss.fork = f;
-    ss.join = j;
-    ss.s = s;
-    return &ss;
-}
 
 // P = 3 or 4, or P = 0 for mixed packs (a.p4mask): then one launch per P, each serving
 // only the experts of its own P.  The two write disjoint rows (an expert's pairs belong
-// to one P), so the P = 3 launch runs on the side stream, forked from and joined back
-// into `st` with events (which graph capture records as dependencies): the two grids
-// share the chip instead of each leaving it part empty at its tail.
+// to one P), so with a side stream the P = 3 launch runs there, forked from and joined
+// back into `st` with the caller's events (which graph capture records as dependencies):
+// the two grids share the chip instead of each leaving it part empty at its tail.
 // Returns false only when the join back into `st` could not be recorded (the caller's
 // later work would not wait for the side stream's launch).
 template <int MODE>
-bool mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
+bool mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, hipStream_t st,
+                   const Side& side = Side()) {
     auto run = [&](int p, hipStream_t s) {
         if (p == 4) {
             if (vec) launch_mfma<4, true, MODE>(a, prefill, gridy, s);
@@ -1190,18 +1174,14 @@ bool mfma_dispatch(int P, bool vec, const MfmaArgs& a, bool prefill, int gridy, 
         run(P, st);
         return true;
     }
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* ss = side_stream(st);
-    if (!ss || hipEventRecord(ss->fork, st) != hipSuccess ||
-        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+    if (!side.on() || !side.fork_from(st)) {
         run(4, st);
         run(3, st);
         return true;
     }
-    run(3, ss->s);
+    run(3, side.s);
     run(4, st);
-    return hipEventRecord(ss->join, ss->s) == hipSuccess &&
-           hipStreamWaitEvent(st, ss->join, 0) == hipSuccess;
+    return side.join_into(st);
 }
 
 // Split point of a multi-token call: experts e < E * kSplitNum / kSplitDen on the caller's
@@ -1233,7 +1213,7 @@ bool moe_layout(int T, int top_k, int E, int H, int I, MoeLayout* L) {
 
 extern "C" {
 
-int seedmm_version(void) { return 100; }
+int seedmm_version(void) { return 200; }
 
 const char* seedmm_strerror(int status) {
     switch (status) {
@@ -1257,11 +1237,11 @@ int seedmm_gemv_ex(const uint16_t* seeds, const uint16_t* coefs, const uint8_t* 
     if (!seeds || !coefs || !codes || !x || !y) return SEEDMM_EINVAL;
     if (!aligned16(x)) return SEEDMM_EALIGN;
     hipStream_t st = (hipStream_t)hip_stream;
-    if (K == 0) {   // empty product: y = 0
-        for (int n = 0; n < N; ++n)
-            if (hipMemsetAsync(y + (int64_t)n * ldy, 0, sizeof(float) * (size_t)M, st) != hipSuccess)
-                return SEEDMM_EHIP;
-        return SEEDMM_OK;
+    if (K == 0) {   // empty product: y = 0 (a kernel, not a memset node, under capture)
+        const int64_t n = (int64_t)N * M;
+        hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y,
+                           ldy, M, n);
+        return launch_status();
     }
     if (x_dtype == SEEDMM_F32) {
         if (ldx % 4 != 0) return SEEDMM_EALIGN;
@@ -1334,7 +1314,8 @@ namespace seedmm_layer {
 int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
             float* y, int E, int H, int I, int P, const uint32_t* p4mask, seedmm_mat gate,
             seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
-            void* hip_stream, void* const* events, const int32_t* slot, int64_t slot_stride) {
+            void* hip_stream, void* const* events, const int32_t* slot, int64_t slot_stride,
+            const seedmm_side* side) {
     if (T < 0 || E < 1 || E > 4096 || top_k < 1 || top_k > E || top_k > 64) return SEEDMM_EINVAL;
     if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0) return SEEDMM_EINVAL;
     if (P == 0 ? !p4mask : (P != 3 && P != 4)) return SEEDMM_EINVAL;
@@ -1351,6 +1332,13 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     if (!workspace || workspace_bytes < L.total) return SEEDMM_EWORKSPACE;
     if (!aligned16(workspace)) return SEEDMM_EALIGN;
     hipStream_t st = (hipStream_t)hip_stream;
+    Side sd;
+    if (side && side->stream) {
+        if (!side->fork || !side->join || side->stream == hip_stream) return SEEDMM_EINVAL;
+        sd.s = (hipStream_t)side->stream;
+        sd.fork = (hipEvent_t)side->fork;
+        sd.join = (hipEvent_t)side->join;
+    }
     char* ws = (char*)workspace;
     int32_t* counts = (int32_t*)(ws + L.counts);
     int32_t* lists = (int32_t*)(ws + L.lists);
@@ -1409,41 +1397,35 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     b.slot = slot;
     b.slot_stride = slot_stride;
 
-    // Several tokens, one P: the experts below `cut` run their gate/up and down launches
-    // on the caller's stream, the others on the library's side stream (forked and joined
-    // with events, which graph capture records as dependencies).  Each launch ends in a
-    // partly empty last round of workgroups (for the prefill kernel, one workgroup per CU
-    // and ~16 per expert, most of the chip), and down cannot start before gate/up has
-    // drained; with two streams the other half's workgroups fill those gaps.  Timed calls
-    // (events) keep the single-stream order.
+    // Several tokens, one P, and a side stream from the caller: the experts below `cut`
+    // run their gate/up and down launches on hip_stream, the others on the side stream
+    // (forked and joined with the caller's events, which graph capture records as
+    // dependencies).  Each launch ends in a partly empty last round of workgroups (for
+    // the prefill kernel, one workgroup per CU and ~16 per expert, most of the chip), and
+    // down cannot start before gate/up has drained; with two streams the other half's
+    // workgroups fill those gaps.  Timed calls (events) keep the single-stream order.
     bool split = false, joined = true;
-    if (!one && P != 0 && !events && E >= 2) {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream* ss = side_stream(st);
-        if (ss && hipEventRecord(ss->fork, st) == hipSuccess &&
-            hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
-            const int cut = (int)((int64_t)E * kSplitNum / kSplitDen);
-            MfmaArgs pa[2] = {a, a}, pb[2] = {b, b};
-            int gy[2];
-            for (int part = 0; part < 2; ++part) {
-                pa[part].e_lo = pb[part].e_lo = part ? cut : 0;
-                pa[part].e_hi = pb[part].e_hi = part ? E : cut;
-                const int ne = pa[part].e_hi - pa[part].e_lo;
-                gy[part] = pairs < ne ? pairs : ne;
-            }
-            mfma_dispatch<MODE_GATEUP>(P, vec, pa[0], prefill, gy[0], st);
-            mfma_dispatch<MODE_GATEUP>(P, vec, pa[1], prefill, gy[1], ss->s);
-            mfma_dispatch<MODE_DOWN>(P, vec, pb[0], prefill, gy[0], st);
-            mfma_dispatch<MODE_DOWN>(P, vec, pb[1], prefill, gy[1], ss->s);
-            joined = hipEventRecord(ss->join, ss->s) == hipSuccess &&
-                     hipStreamWaitEvent(st, ss->join, 0) == hipSuccess;
-            split = true;
+    if (!one && P != 0 && !events && E >= 2 && sd.on() && sd.fork_from(st)) {
+        const int cut = (int)((int64_t)E * kSplitNum / kSplitDen);
+        MfmaArgs pa[2] = {a, a}, pb[2] = {b, b};
+        int gy[2];
+        for (int part = 0; part < 2; ++part) {
+            pa[part].e_lo = pb[part].e_lo = part ? cut : 0;
+            pa[part].e_hi = pb[part].e_hi = part ? E : cut;
+            const int ne = pa[part].e_hi - pa[part].e_lo;
+            gy[part] = pairs < ne ? pairs : ne;
         }
+        mfma_dispatch<MODE_GATEUP>(P, vec, pa[0], prefill, gy[0], st);
+        mfma_dispatch<MODE_GATEUP>(P, vec, pa[1], prefill, gy[1], sd.s);
+        mfma_dispatch<MODE_DOWN>(P, vec, pb[0], prefill, gy[0], st);
+        mfma_dispatch<MODE_DOWN>(P, vec, pb[1], prefill, gy[1], sd.s);
+        joined = sd.join_into(st);
+        split = true;
     }
     if (!split) {
-        joined = mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st);
+        joined = mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st, events ? Side() : sd);
         mark(2);
-        joined = mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st) && joined;
+        joined = mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st, events ? Side() : sd) && joined;
         mark(3);
     }
     // without the join the combine could read outputs still being written: report it
@@ -1470,7 +1452,16 @@ int seedmm_moe_timed(const int32_t* topk_ids, const float* topk_w, int T, int to
                      void* hip_stream, void* const* events) {
     if (P != 3 && P != 4) return SEEDMM_EINVAL;
     return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, P, nullptr, gate, up, down,
-                   workspace, workspace_bytes, hip_stream, events, nullptr, 0);
+                   workspace, workspace_bytes, hip_stream, events, nullptr, 0, nullptr);
+}
+
+int seedmm_moe_ex(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,
+                  float* y, int E, int H, int I, int P, const uint32_t* p4mask, seedmm_mat gate,
+                  seedmm_mat up, seedmm_mat down, void* workspace, size_t workspace_bytes,
+                  void* hip_stream, const seedmm_side* side) {
+    if (P == 0 ? !p4mask : ((P != 3 && P != 4) || p4mask)) return SEEDMM_EINVAL;
+    return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, P, p4mask, gate, up, down,
+                   workspace, workspace_bytes, hip_stream, nullptr, nullptr, 0, side);
 }
 
 int seedmm_moe_mixed(const int32_t* topk_ids, const float* topk_w, int T, int top_k,
@@ -1479,7 +1470,7 @@ int seedmm_moe_mixed(const int32_t* topk_ids, const float* topk_w, int T, int to
                      size_t workspace_bytes, void* hip_stream) {
     if (!p4mask) return SEEDMM_EINVAL;
     return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, 0, p4mask, gate, up, down,
-                   workspace, workspace_bytes, hip_stream, nullptr, nullptr, 0);
+                   workspace, workspace_bytes, hip_stream, nullptr, nullptr, 0, nullptr);
 }
 
 int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, const void* x,

@@ -1,7 +1,8 @@
 """Thin Python binding of the seedmm C ABI (include/seedmm.h).
 
 Argument marshalling only: tensors are passed to the HIP library as device pointers
-plus sizes, on torch's current HIP stream.  Every step of the computation runs in
+plus sizes, on torch's current HIP stream or the one passed in (outputs and scratch the
+binding allocates belong to that stream).  Every step of the computation runs in
 the library's kernels; there is no Python or CPU fallback, and a missing library
 raises at import.
 """
@@ -30,6 +31,11 @@ class SeedMat(ctypes.Structure):
                 ("codes", ctypes.c_void_p), ("exp_bias", ctypes.c_void_p)]
 
 
+class SeedSide(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("fork", ctypes.c_void_p),
+                ("join", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -46,7 +52,12 @@ def _load():
     L.seedmm_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, SeedMat, SeedMat, SeedMat,
                              p, ctypes.c_size_t, p]
     L.seedmm_moe_timed.argtypes = L.seedmm_moe.argtypes + [p]
-    L.seedmm_search.argtypes = [p, i32, p, i32, i32, i32, ctypes.c_int32, p, p, p, p, p]
+    L.seedmm_moe_ex.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, p, SeedMat, SeedMat,
+                                SeedMat, p, ctypes.c_size_t, p, ctypes.POINTER(SeedSide)]
+    L.seedmm_search.argtypes = [p, i32, p, i32, i32, i32, ctypes.c_int32, p, p, p, p, p, p]
+    L.seedmm_search_table_bytes.restype = ctypes.c_size_t
+    L.seedmm_search_table_bytes.argtypes = [i32]
+    L.seedmm_search_prepare.argtypes = [i32, p, ctypes.c_size_t, p]
     L.seedmm_moe_mixed.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, p, SeedMat, SeedMat,
                                    SeedMat, p, ctypes.c_size_t, p]
     sz = ctypes.c_size_t
@@ -65,7 +76,8 @@ def _load():
     L.seedmm_strerror.argtypes = [i32]
     L.seedmm_version.restype = i32
     for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-                 "seedmm_moe", "seedmm_moe_timed", "seedmm_search", "seedmm_moe_mixed",
+                 "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_ex", "seedmm_search",
+                 "seedmm_search_prepare", "seedmm_moe_mixed",
                  "seedmm_cache_init", "seedmm_cache_reset", "seedmm_cache_plan",
                  "seedmm_cache_moe", "seedmm_cache_stats"):
         getattr(L, name).restype = i32
@@ -75,8 +87,9 @@ def _load():
 _lib = _load()
 
 EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_mixed",
-           "seedmm_search", "seedmm_cache_record_layout", "seedmm_cache_state_bytes",
+           "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_ex",
+           "seedmm_moe_mixed", "seedmm_search", "seedmm_search_table_bytes",
+           "seedmm_search_prepare", "seedmm_cache_record_layout", "seedmm_cache_state_bytes",
            "seedmm_cache_device_bytes",
            "seedmm_cache_init", "seedmm_cache_reset", "seedmm_cache_plan", "seedmm_cache_moe",
            "seedmm_cache_stats", "seedmm_strerror", "seedmm_version")
@@ -98,6 +111,40 @@ def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(stream):
+    """Allocation context: new tensors belong to `stream` (None: the current stream), so
+    the caching allocator does not hand their memory to other streams while the
+    library's kernels on `stream` may still use it."""
+    return torch.cuda.stream(stream) if stream is not None else _Nothing()
+
+
+class _Nothing:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
+
+
+class SideStream:
+    """A second stream of one device and its fork / join events, for moe(side=...) and
+    moe_mixed(side=...): the layer runs one half of its expert launches there
+    (seedmm_moe_ex).  Owned by the caller; concurrent layer calls need one each."""
+
+    def __init__(self, device=None):
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.stream = torch.cuda.Stream(device=dev)          # default priority
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        # torch creates an event on its first record: record both once so handles exist
+        self.fork.record(self.stream)
+        self.join.record(self.stream)
+        self.stream.synchronize()
+
+    def c(self) -> SeedSide:
+        return SeedSide(self.stream.cuda_stream, self.fork.cuda_event, self.join.cuda_event)
 
 
 def _check(status: int, what: str):
@@ -182,7 +229,8 @@ def gemv_ex(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor 
     if ldx < K:
         raise ValueError(f"x rows hold {ldx} elements, K = {K}")
     if y is None:
-        y = torch.empty((N, M), dtype=torch.float32, device=x.device)
+        with _on(stream):
+            y = torch.empty((N, M), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
     if y.shape[-1] < M or y.numel() < N * y.shape[-1]:
         raise ValueError(f"y must hold [{N}][{M}]")
@@ -199,7 +247,8 @@ def reconstruct(mat: dict, M: int, K: int, P: int, dtype=torch.float32, out=None
     _check_streams(mat, 1, M, K, P, "W")
     dev = mat["seeds"].device
     if out is None:
-        out = torch.empty((M, K), dtype=dtype, device=dev)
+        with _on(stream):
+            out = torch.empty((M, K), dtype=dtype, device=dev)
     _dev(out, dtype, "W")
     _check_numel(out, M * K, "W")
     eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
@@ -213,8 +262,9 @@ def moe_dispatch(topk_ids: torch.Tensor, E: int, stream=None):
     """(counts int32[E], lists int32[E][T]) for topk_ids int32 [T][top_k]."""
     _dev(topk_ids, torch.int32, "topk_ids")
     T, k = topk_ids.shape
-    counts = torch.empty(E, dtype=torch.int32, device=topk_ids.device)
-    lists = torch.full((E, max(T, 1)), -1, dtype=torch.int32, device=topk_ids.device)
+    with _on(stream):
+        counts = torch.empty(E, dtype=torch.int32, device=topk_ids.device)
+        lists = torch.full((E, max(T, 1)), -1, dtype=torch.int32, device=topk_ids.device)
     _check(_lib.seedmm_moe_dispatch(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(lists),
                                     _stream(stream)), "seedmm_moe_dispatch")
     return counts, lists
@@ -239,30 +289,38 @@ def _check_layer(T, k, topk_w, x, E, H, I, Ps, gate, up, down, exact_coefs=True)
 
 
 def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None, stream=None,
-        events=None):
+        events=None, side=None):
     """Routed SwiGLU MoE layer (seedmm_moe); x bf16 [T][H] -> y fp32 [T][H].
     `events`: optional 5 raw hipEvent_t handles (ints) recorded between the stages
-    (seedmm_moe_timed)."""
+    (seedmm_moe_timed).  `side`: optional SideStream for the second half of the expert
+    launches (seedmm_moe_ex)."""
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")
     T, k = topk_ids.shape
     _check_layer(T, k, topk_w, x, E, H, I, P, gate, up, down)
-    if y is None:
-        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if events is not None and side is not None:
+        raise ValueError("the timed layer call runs on one stream (no side stream)")
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+        need = moe_workspace_bytes(T, k, E, H, I)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _dev(y, torch.float32, "y")
     _check_numel(y, T * H, "y")
-    need = moe_workspace_bytes(T, k, E, H, I)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     args = (_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I, P,
             _seedmat(gate), _seedmat(up), _seedmat(down), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    if events is None:
-        _check(_lib.seedmm_moe(*args), "seedmm_moe")
-    else:
+    if events is not None:
         arr = (ctypes.c_void_p * 5)(*[getattr(ev, "cuda_event", ev) for ev in events])
         _check(_lib.seedmm_moe_timed(*args, arr), "seedmm_moe_timed")
+    elif side is not None:
+        sd = side.c()
+        _check(_lib.seedmm_moe_ex(*args[:10], None, *args[10:], ctypes.byref(sd)),
+               "seedmm_moe_ex")
+    else:
+        _check(_lib.seedmm_moe(*args), "seedmm_moe")
     return y
 
 
@@ -280,10 +338,11 @@ def p4_mask(Ps, device) -> torch.Tensor:
 
 
 def moe_mixed(topk_ids, topk_w, x, E, H, I, p4mask, gate, up, down, y=None, workspace=None,
-              stream=None, Ps=None):
+              stream=None, Ps=None, side=None):
     """Routed SwiGLU MoE layer with P chosen per expert (seedmm_moe_mixed); p4mask from
     p4_mask(Ps).  Given Ps, the coefficient streams are checked against it; without, only
-    the seed and code streams are (the mask lives on the device)."""
+    the seed and code streams are (the mask lives on the device).  `side`: optional
+    SideStream for the P = 3 launches (seedmm_moe_ex with P = 0)."""
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")
@@ -292,17 +351,48 @@ def moe_mixed(topk_ids, topk_w, x, E, H, I, p4mask, gate, up, down, y=None, work
     T, k = topk_ids.shape
     _check_layer(T, k, topk_w, x, E, H, I, Ps if Ps is not None else 3, gate, up, down,
                  exact_coefs=Ps is not None)
-    if y is None:
-        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+                                    device=x.device)
     _dev(y, torch.float32, "y")
-    if workspace is None:
-        workspace = torch.empty(moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
-                                device=x.device)
-    _check(_lib.seedmm_moe_mixed(_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I,
-                                 _ptr(p4mask), _seedmat(gate), _seedmat(up), _seedmat(down),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(stream)), "seedmm_moe_mixed")
+    _check_numel(y, T * H, "y")
+    args = (_ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y), E, H, I)
+    rest = (_seedmat(gate), _seedmat(up), _seedmat(down), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if side is not None:
+        sd = side.c()
+        _check(_lib.seedmm_moe_ex(*args, 0, _ptr(p4mask), *rest, ctypes.byref(sd)),
+               "seedmm_moe_ex")
+    else:
+        _check(_lib.seedmm_moe_mixed(*args, _ptr(p4mask), *rest), "seedmm_moe_mixed")
     return y
+
+
+_TABLES = {}
+
+
+def search_table(P: int, device=None, stream=None):
+    """The encoder's per-seed table for P on a device (seedmm_search_prepare), filled
+    once and kept by this module for later searches on that device."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = (dev.index, int(P))
+    if key not in _TABLES:
+        n = int(_lib.seedmm_search_table_bytes(P))
+        if n == 0:
+            raise SeedmmError(EINVAL, "seedmm_search_table_bytes")
+        with _on(stream):
+            buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        off = (-buf.data_ptr()) % 256
+        tab = buf[off:off + n]
+        _check(_lib.seedmm_search_prepare(P, _ptr(tab), n, _stream(stream)),
+               "seedmm_search_prepare")
+        # later searches may run on other streams: wait for the fill once, here
+        (stream or torch.cuda.current_stream()).synchronize()
+        _TABLES[key] = (buf, tab)
+    return _TABLES[key][1]
 
 
 def search(W: torch.Tensor, P: int, exp_bias: int, colw: torch.Tensor = None, err=True,
@@ -317,16 +407,16 @@ def search(W: torch.Tensor, P: int, exp_bias: int, colw: torch.Tensor = None, er
         _check_numel(colw, K, "colw")
     nblk = M * (K // 8)
     dev = W.device
-    out = {"seeds": torch.empty(nblk, dtype=torch.uint16, device=dev),
-           "coefs": torch.empty((nblk * P + 3) // 4, dtype=torch.uint16, device=dev),
-           "codes": torch.empty((nblk + 1) // 2, dtype=torch.uint8, device=dev),
-           "exp_bias": torch.full((1,), exp_bias, dtype=torch.int32, device=dev),
-           "exp_bias_host": [exp_bias]}
-    e = torch.empty(nblk, dtype=torch.float64, device=dev) if err else None
-    if colw is not None:
-        _dev(colw, torch.float32, "colw")
+    table = search_table(P, dev, stream) if colw is None else None
+    with _on(stream):
+        out = {"seeds": torch.empty(nblk, dtype=torch.uint16, device=dev),
+               "coefs": torch.empty((nblk * P + 3) // 4, dtype=torch.uint16, device=dev),
+               "codes": torch.empty((nblk + 1) // 2, dtype=torch.uint8, device=dev),
+               "exp_bias": torch.full((1,), exp_bias, dtype=torch.int32, device=dev),
+               "exp_bias_host": [exp_bias]}
+        e = torch.empty(nblk, dtype=torch.float64, device=dev) if err else None
     _check(_lib.seedmm_search(_ptr(W), K, _ptr(colw), M, K, P, exp_bias, _ptr(out["seeds"]),
-                              _ptr(out["coefs"]), _ptr(out["codes"]), _ptr(e),
+                              _ptr(out["coefs"]), _ptr(out["codes"]), _ptr(e), _ptr(table),
                               _stream(stream)), "seedmm_search")
     if err:
         out["err"] = e
@@ -411,12 +501,13 @@ class ExpertCache:
         T, k = topk_ids.shape
         if ids_h.shape != (T, k):
             raise ValueError("topk_ids_host and topk_ids differ in shape")
-        if y is None:
-            y = torch.empty((T, self.H), dtype=torch.float32, device=x.device)
+        with _on(stream):
+            if y is None:
+                y = torch.empty((T, self.H), dtype=torch.float32, device=x.device)
+            if workspace is None:
+                workspace = torch.empty(moe_workspace_bytes(T, k, self.E, self.H, self.I),
+                                        dtype=torch.uint8, device=x.device)
         _dev(y, torch.float32, "y")
-        if workspace is None:
-            workspace = torch.empty(moe_workspace_bytes(T, k, self.E, self.H, self.I),
-                                    dtype=torch.uint8, device=x.device)
         _check(_lib.seedmm_cache_moe(self.handle, ids_h.ctypes.data_as(ctypes.c_void_p),
                                      _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y),
                                      _ptr(workspace),

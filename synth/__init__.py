@@ -11,7 +11,8 @@ Recipe:
   * coefficient nibbles uniform in [-8, 7] and exponent codes uniform in [0, 15];
     both are uniform 4-bit fields, so their packed streams are uniform random words
     and bytes of the stream lengths below;
-  * exp_bias = -4 for every matrix;
+  * exp_bias = -4 for every matrix, or per matrix values chosen by a test (a stacked
+    tensor holds one exp_bias per matrix);
   * activations x ~ N(0, 1) (Box-Muller in float64, then fp32, then bf16 by
     round-to-nearest-even where the workload uses bf16);
   * router logits ~ N(0, 1) fp32 [T][E]; top-k by logit (ties to the lower expert id),
@@ -26,7 +27,7 @@ import numpy as np
 __all__ = [
     "splitmix64", "uniform_u64", "stream_lengths", "seed_matrix", "normal_f32",
     "bf16_bits", "bf16_bits_to_f32", "route_topk", "hot_bias", "config_seed",
-    "seed_matrix_mixed",
+    "seed_matrix_mixed", "plant_degenerate", "uniform_ints",
 ]
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -67,12 +68,12 @@ def stream_lengths(nblk: int, P: int):
     return nblk, (nblk * P + 3) // 4, (nblk + 1) // 2
 
 
-def seed_matrix(base: int, tag: str, M: int, K: int, P: int, E: int = 1, exp_bias: int = -4):
+def seed_matrix(base: int, tag: str, M: int, K: int, P: int, E: int = 1, exp_bias=-4):
     """Random seed-coded streams for E stacked [M][K] matrices.
 
-    Returns dict(seeds u16, coefs u16, codes u8, exp_bias i32[E]).  Each expert's
-    streams are whole words/bytes (requires (M*K/8)*P % 4 == 0 and (M*K/8) % 2 == 0
-    when E > 1)."""
+    Returns dict(seeds u16, coefs u16, codes u8, exp_bias i32[E]).  exp_bias is one
+    value for every matrix or a sequence of E values.  Each expert's streams are whole
+    words/bytes (requires (M*K/8)*P % 4 == 0 and (M*K/8) % 2 == 0 when E > 1)."""
     assert K % 8 == 0
     nblk1 = M * (K // 8)
     if E > 1:
@@ -83,8 +84,37 @@ def seed_matrix(base: int, tag: str, M: int, K: int, P: int, E: int = 1, exp_bia
     seeds = (r % np.uint64(65535) + np.uint64(1)).astype(np.uint16)
     coefs = (uniform_u64(base, tag + ".coefs", nc) >> np.uint64(48)).astype(np.uint16)
     codes = (uniform_u64(base, tag + ".codes", nd) >> np.uint64(56)).astype(np.uint8)
-    eb = np.full(E, exp_bias, dtype=np.int32)
+    eb = np.asarray(exp_bias, dtype=np.int64)
+    eb = np.full(E, int(eb), dtype=np.int32) if eb.ndim == 0 else eb.astype(np.int32).reshape(E)
     return {"seeds": seeds, "coefs": coefs, "codes": codes, "exp_bias": eb}
+
+
+def uniform_ints(base: int, tag: str, n: int, lo: int, hi: int) -> np.ndarray:
+    """n integers uniform in [lo, hi] (int64)."""
+    r = uniform_u64(base, tag, n)
+    return (r % np.uint64(hi - lo + 1)).astype(np.int64) + lo
+
+
+def plant_degenerate(mat: dict, P: int, base: int, tag: str, frac: float = 0.02) -> dict:
+    """A copy of `mat` with degenerate blocks planted at seeded random places: seed 0 in
+    about `frac` of the blocks, and all-zero coefficient words for about `frac` of the
+    aligned groups of 4 blocks (a group's P*4 nibbles fill P whole words).  Returns the
+    copy; its 'seed0' and 'zero_groups' entries list the planted block and group indices."""
+    out = {k: np.array(v, copy=True) for k, v in mat.items()}
+    nblk = out["seeds"].size
+    n0 = max(1, int(nblk * frac))
+    b0 = np.unique((uniform_u64(base, tag + ".seed0", n0) % np.uint64(nblk)).astype(np.int64))
+    out["seeds"][b0] = 0
+    ngroups = nblk // 4
+    groups = np.zeros(0, dtype=np.int64)
+    if ngroups:
+        ng = max(1, int(ngroups * frac))
+        groups = np.unique((uniform_u64(base, tag + ".zero", ng) % np.uint64(ngroups)).astype(np.int64))
+        for g in groups:
+            out["coefs"][g * P:(g + 1) * P] = 0
+    out["seed0"] = b0
+    out["zero_groups"] = groups
+    return out
 
 
 def seed_matrix_mixed(base: int, tag: str, M: int, K: int, Ps, exp_bias: int = -4):

@@ -120,14 +120,44 @@ def test_binding_has_no_fallback():
 
 def test_search_rejects(lib):
     f = lib.seedmm_search
-    # (W, ldw, colw, M, K, P, exp_bias, seeds, coefs, codes, err, stream)
-    assert f(FAKE, 12, None, 4, 12, 4, -4, FAKE, FAKE, FAKE, None, None) == -1    # K % 8
-    assert f(FAKE, 16, None, 4, 16, 5, -4, FAKE, FAKE, FAKE, None, None) == -1    # P
-    assert f(FAKE, 16, None, 4, 16, 4, 101, FAKE, FAKE, FAKE, None, None) == -1   # exp_bias
-    assert f(FAKE, 8, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, None) == -1     # ldw < K
-    assert f(None, 16, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, None) == -1    # null W
-    assert f(FAKE, 16, None, 4, 16, 4, -4, FAKE, None, FAKE, None, None) == -1    # null coefs
-    assert f(None, 16, None, 0, 16, 4, -4, None, None, None, None, None) == 0     # empty
+    # (W, ldw, colw, M, K, P, exp_bias, seeds, coefs, codes, err, table, stream)
+    T = FAKE   # a 256-byte aligned table address, never dereferenced
+    assert f(FAKE, 12, None, 4, 12, 4, -4, FAKE, FAKE, FAKE, None, T, None) == -1    # K % 8
+    assert f(FAKE, 16, None, 4, 16, 5, -4, FAKE, FAKE, FAKE, None, T, None) == -1    # P
+    assert f(FAKE, 16, None, 4, 16, 4, 101, FAKE, FAKE, FAKE, None, T, None) == -1   # exp_bias
+    assert f(FAKE, 8, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, T, None) == -1     # ldw < K
+    assert f(None, 16, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, T, None) == -1    # null W
+    assert f(FAKE, 16, None, 4, 16, 4, -4, FAKE, None, FAKE, None, T, None) == -1    # null coefs
+    assert f(FAKE, 16, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, None, None) == -1  # no table
+    assert f(FAKE, 16, None, 4, 16, 4, -4, FAKE, FAKE, FAKE, None, T + 16, None) == -2  # table align
+    assert f(None, 16, None, 0, 16, 4, -4, None, None, None, None, None, None) == 0  # empty
+
+
+def test_search_table_size_and_prepare_rejects(lib):
+    n4, n3 = lib.seedmm_search_table_bytes(4), lib.seedmm_search_table_bytes(3)
+    assert n4 > n3 > 8_000_000 and n4 % 256 == 0 and n3 % 256 == 0
+    assert lib.seedmm_search_table_bytes(5) == 0
+    g = lib.seedmm_search_prepare
+    assert g(5, FAKE, n4, None) == -1           # P
+    assert g(4, None, n4, None) == -1           # null table
+    assert g(4, FAKE, n4 - 1, None) == -1       # too small
+    assert g(4, FAKE + 16, n4, None) == -2      # alignment
+
+
+def test_moe_ex_rejects(lib):
+    from pseudo_random_weight_amd.seedmm import SeedMat, SeedSide
+    m = SeedMat(FAKE, FAKE, FAKE, FAKE)
+    ws = lib.seedmm_moe_workspace_bytes(4, 2, 8, 64, 64)
+    f = lib.seedmm_moe_ex
+
+    def call(P=4, mask=None, side=None):
+        return f(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 64, 64, P, mask, m, m, m, FAKE, ws, FAKE,
+                 None if side is None else ctypes.byref(side))
+    assert call(P=0) == -1                                   # mixed without a mask
+    assert call(P=4, mask=FAKE) == -1                        # a mask with one P
+    assert call(P=5) == -1
+    assert call(side=SeedSide(FAKE + 256, None, FAKE)) == -1  # side stream without a fork
+    assert call(side=SeedSide(FAKE, FAKE, FAKE)) == -1        # side stream = hip_stream
 
 
 def test_moe_mixed_rejects_a_missing_mask(lib):

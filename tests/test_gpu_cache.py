@@ -132,3 +132,41 @@ def test_cache_capacity_error_leaves_the_cache_usable(sm):
                    E, H, I, P, devm["gate"], devm["up"], devm["down"])
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy(), y_ref.cpu().numpy())
+
+
+@pytest.mark.parametrize("P", [4, 3])
+def test_cache_per_expert_biases_and_degenerate_blocks(sm, oracle, P):
+    """Every expert's gate, up and down with an exp_bias of its own (gate outputs of order
+    1, where silu is curved) and planted seed-0 and zero-coefficient blocks: the cached
+    layer reads each expert's biases by expert id, not by slot, so its output equals the
+    resident layer's bit for bit across loads and evictions, and the oracle's within
+    1e-2 (a slot-indexed bias would scale whole experts by powers of two)."""
+    import torch
+    E, H, I, k, S = 12, 256, 128, 2, 4   # a 2-token call touches up to 4 experts
+    say("cache per-expert biases", P)
+    base = synth.config_seed(26)
+    host = {}
+    for n, lo, hi in (("gate", -22, -20), ("up", -22, -18), ("down", -21, -17)):
+        M, K = (I, H) if n != "down" else (H, I)
+        eb = synth.uniform_ints(base, f"cb{P}.{n}.eb", E, lo, hi)
+        m = synth.seed_matrix(base, f"cb{P}.{n}", M, K, P, E, exp_bias=eb)
+        m = synth.plant_degenerate(m, P, base, f"cb{P}.{n}.deg", frac=0.03)
+        host[n] = {key: m[key] for key in ("seeds", "coefs", "codes", "exp_bias")}
+    assert len(set(host["gate"]["exp_bias"].tolist())) > 1
+    devm = {n: _dev(m) for n, m in host.items()}
+    cache = sm.ExpertCache(host, E, H, I, P, S)
+    for i, T in enumerate([1, 1, 2, 1, 1, 2, 1]):
+        ids, w = _route(f"cb{P}.r{i}", T, E, k)
+        x = synth.bf16_bits(synth.normal_f32(base, f"cb{P}.x{i}", (T, H)))
+        xt = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        ids_d, w_d = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+        y = cache.moe(ids, ids_d, w_d, xt)
+        y_ref = sm.moe(ids_d, w_d, xt, E, H, I, P, devm["gate"], devm["up"], devm["down"])
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), y_ref.cpu().numpy().view(np.uint32)), (i, T)
+        ref = oracle.moe(ids, w, synth.bf16_bits_to_f32(x), E, H, I, P,
+                         host["gate"], host["up"], host["down"])
+        err = np.linalg.norm(y.astype(np.float64) - ref) / np.linalg.norm(ref)
+        assert err <= 1e-2, (i, err)
+    assert cache.stats()["misses"] > S

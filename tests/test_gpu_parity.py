@@ -386,11 +386,12 @@ def _raw_events(n):
 
 @pytest.mark.parametrize("E,P,T", [(8, 4, 600), (7, 3, 600), (12, 4, 16), (5, 3, 9)])
 def test_moe_prefill_two_streams(sm, oracle, E, P, T):
-    """A layer call over several tokens with one P runs each half of the experts on its
-    own stream (caller's and side stream), for the prefill kernels (T = 600 here) and the
-    decode ones (T = 16, 9).  Its output equals the single-stream order of the timed call
-    bit for bit (every expert served exactly once, whatever the split point), matches the
-    oracle, and graph replays of it reproduce the eager result bit for bit."""
+    """A layer call over several tokens with one P and a caller's side stream
+    (seedmm_moe_ex) runs each half of the experts on its own stream, for the prefill
+    kernels (T = 600 here) and the decode ones (T = 16, 9).  Its output equals the
+    single-stream order of the timed call bit for bit (every expert served exactly once,
+    whatever the split point), matches the oracle, and graph replays of it reproduce the
+    eager result bit for bit."""
     import torch
     H, I, k = 256, 256, 2
     say("moe two streams", E, P, T)
@@ -399,7 +400,8 @@ def test_moe_prefill_two_streams(sm, oracle, E, P, T):
     ids_t, w_t = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
     xt, x32 = bf16_tensor(x)
     ws = torch.empty(sm.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
-    y_two = sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, workspace=ws)
+    side = sm.SideStream()
+    y_two = sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, workspace=ws, side=side)
     torch.cuda.synchronize()
     y_one = sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, events=_raw_events(5))
     torch.cuda.synchronize()
@@ -413,7 +415,7 @@ def test_moe_prefill_two_streams(sm, oracle, E, P, T):
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     G = torch.cuda.CUDAGraph()
     with torch.cuda.graph(G):
-        sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, y=y, workspace=ws)
+        sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, y=y, workspace=ws, side=side)
     other = torch.from_numpy(np.roll(ids, 1, axis=0)).cuda()
     for rep in range(3):
         y.fill_(float("nan"))
@@ -421,8 +423,41 @@ def test_moe_prefill_two_streams(sm, oracle, E, P, T):
         G.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint32), y_two.view(np.uint32)), rep
-        sm.moe(other, w_t, xt, E, H, I, P, g, u, d, y=torch.empty_like(y), workspace=ws)
+        # eager work between replays, on the same workspace and side stream
+        sm.moe(other, w_t, xt, E, H, I, P, g, u, d, y=torch.empty_like(y), workspace=ws,
+               side=side)
         torch.cuda.synchronize()
+    # without a side stream (seedmm_moe): the same bits
+    y_plain = sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_plain.cpu().numpy().view(np.uint32), y_two.view(np.uint32))
+
+
+def test_moe_on_a_non_current_stream(sm):
+    """A layer call on a stream other than torch's current one, with the output and the
+    workspace allocated by the binding (on that stream) and a side stream: the result
+    equals the call on the current stream bit for bit, also when the allocator reuses
+    freed blocks between calls."""
+    import torch
+    E, H, I, P, k, T = 12, 256, 256, 4, 2, 40
+    say("moe non-current stream")
+    gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 5, "ncs")
+    g, u, d = dev(gate), dev(up), dev(down)
+    ids_t, w_t = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    xt, _ = bf16_tensor(x)
+    y_ref = sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d).cpu().numpy()
+    s = torch.cuda.Stream()
+    side = sm.SideStream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        y = sm.moe(ids_t, w_t, xt, E, H, I, P, g, u, d, stream=s, side=side if rep else None)
+        outs.append(y)
+        junk = torch.full((1 << 20,), rep, dtype=torch.float32, device="cuda")   # allocator churn
+        del junk
+    s.synchronize()
+    for y in outs:
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
 def test_moe_prefill_full_size_sampled(sm, oracle):
@@ -678,9 +713,10 @@ def test_moe_mixed_with_one_p_is_the_uniform_layer(sm, P, T):
 
 
 def test_moe_mixed_graph_replays_match_eager(sm):
-    """The mixed layer (its P = 3 launches forked onto a second stream and joined back)
-    captured in a HIP graph: every replay, with eager work and synchronisations between
-    replays, gives the eager result bit for bit."""
+    """The mixed layer with a side stream (its P = 3 launches forked onto the caller's
+    second stream and joined back) captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, gives the eager single-stream result bit for
+    bit."""
     import torch
     E, H, I, k, T = 100, 2048, 1024, 8, 16
     Ps = [4 if v else 3 for v in (synth.uniform_u64(synth.config_seed(10), "mix.P", E) & np.uint64(1))]
@@ -696,8 +732,9 @@ def test_moe_mixed_graph_replays_match_eager(sm):
     xt, _ = bf16_tensor(x)
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(sm.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    two = sm.SideStream()
     call = lambda ids_in, y_out: sm.moe_mixed(ids_in, w_t, xt, E, H, I, mask, g, u, d, Ps=Ps,
-                                              y=y_out, workspace=ws)
+                                              y=y_out, workspace=ws, side=two)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):

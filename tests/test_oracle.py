@@ -510,3 +510,66 @@ def test_moe_mixed_is_the_slot_sum_of_each_experts_own_ffn(oracle):
             ref += float(w[t, s]) * oracle.expert(parts["gate"][e], parts["up"][e], parts["down"][e],
                                                   x[t:t + 1], H, I, Ps[e])[0].astype(np.float64)
         np.testing.assert_allclose(y[t], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
+
+
+def test_seed_zero_block_is_constant(oracle):
+    # every state of seed 0 is 0, so every basis value is -32768 and the 8 weights of the
+    # block are 2^(code + exp_bias - 15) * (-32768) * sum_j c_j
+    for P, c, code, eb in ((4, [3, -8, 7, 1], 9, -4), (3, [-5, 2, 6, 0], 15, -20), (4, [0, 0, 0, 0], 4, 0)):
+        w = oracle.block(0, c, P, code, eb)
+        expect = -32768.0 * sum(c[:P]) * 2.0 ** (code + eb - 15)
+        assert np.all(w.astype(np.float64) == expect), (w, expect)
+
+
+def test_silu_in_its_curved_range(oracle):
+    # a gate at exp_bias -21 gives gate outputs of order 1: the expert equals the float64
+    # composition with silu(z) = z / (1 + e^-z) evaluated where it is far from relu
+    H, I, T, P = 256, 64, 4, 4
+    base = synth.config_seed(24)
+    gate = synth.seed_matrix(base, "cg", I, H, P, exp_bias=-21)
+    up = synth.seed_matrix(base, "cu", I, H, P, exp_bias=-19)
+    down = synth.seed_matrix(base, "cd", H, I, P, exp_bias=-18)
+    x = synth.bf16_bits_to_f32(synth.bf16_bits(synth.normal_f32(base, "cx", (T, H))))
+    Wg = oracle.reconstruct_f32(gate, I, H, P).astype(np.float64)
+    g = x.astype(np.float64) @ Wg.T
+    assert np.mean(np.abs(g) < 4.0) > 0.5 and np.mean(np.abs(g) < 0.5) > 0.05
+    # closed-form values of silu at 0, +-1 and +-2
+    for z, s in ((0.0, 0.0), (1.0, 0.7310585786300049), (-1.0, -0.2689414213699951),
+                 (2.0, 1.7615941559557649), (-2.0, -0.2384058440442351)):
+        assert abs(z / (1.0 + np.exp(-z)) - s) < 1e-15
+    Wu = oracle.reconstruct_f32(up, I, H, P).astype(np.float64)
+    Wd = oracle.reconstruct_f32(down, H, I, P).astype(np.float64)
+    ref = _np_expert(Wg, Wu, Wd, x.astype(np.float64))
+    got = oracle.expert(gate, up, down, x, H, I, P)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-9 * np.abs(ref).max())
+    # relu in place of silu would be far off here (a dropped exponential is caught)
+    relu = (np.maximum(g, 0.0) * (x.astype(np.float64) @ Wu.T)) @ Wd.T
+    assert np.linalg.norm(relu - ref) > 0.05 * np.linalg.norm(ref)
+
+
+def test_moe_reads_each_matrix_own_exp_bias(oracle):
+    # per-expert biases that differ between gate, up and down: the layer equals the
+    # weighted sum of each expert computed from its own three single matrices
+    E, H, I, T, k, P = 4, 64, 32, 5, 2, 4
+    base = synth.config_seed(25)
+    ebs = {"g": [-21, -20, -22, -19], "u": [-18, -22, -20, -21], "d": [-17, -19, -21, -20]}
+    gate = synth.seed_matrix(base, "bg", I, H, P, E, exp_bias=ebs["g"])
+    up = synth.seed_matrix(base, "bu", I, H, P, E, exp_bias=ebs["u"])
+    down = synth.seed_matrix(base, "bd", H, I, P, E, exp_bias=ebs["d"])
+    x = synth.bf16_bits_to_f32(synth.bf16_bits(synth.normal_f32(base, "bx", (T, H))))
+    ids, w = synth.route_topk(base, "br", T, E, k)
+    got = oracle.moe(ids, w, x, E, H, I, P, gate, up, down)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for s in range(k):
+            e = int(ids[t, s])
+            mats = []
+            for m, (M, K) in ((gate, (I, H)), (up, (I, H)), (down, (H, I))):
+                n = M * K // 8
+                mats.append(oracle.reconstruct_f32(
+                    {"seeds": m["seeds"][e * n:(e + 1) * n].copy(),
+                     "coefs": m["coefs"][e * n * P // 4:(e + 1) * n * P // 4].copy(),
+                     "codes": m["codes"][e * n // 2:(e + 1) * n // 2].copy(),
+                     "exp_bias": m["exp_bias"][e:e + 1].copy()}, M, K, P).astype(np.float64))
+            ref[t] += w[t, s] * _np_expert(*mats, x[t:t + 1].astype(np.float64))[0]
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
