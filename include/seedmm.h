@@ -60,8 +60,10 @@ enum {
     SEEDMM_EALIGN = -2,     /* activation or output pointer / leading dim misaligned  */
     SEEDMM_EWORKSPACE = -3, /* workspace missing or smaller than seedmm_moe_workspace_bytes */
     SEEDMM_EHIP = -4,       /* the HIP runtime reported a launch failure              */
-    SEEDMM_ECAPACITY = -5   /* an expert cache call routes to more distinct experts
+    SEEDMM_ECAPACITY = -5,  /* an expert cache call routes to more distinct experts
                                than the cache has slots                               */
+    SEEDMM_ESCRATCH = -6    /* seedmm_moe_noalloc: the batch needs more scratch than
+                               SEEDMM_NOALLOC_SCRATCH_BYTES                           */
 };
 
 enum { SEEDMM_F32 = 0, SEEDMM_BF16 = 1 };
@@ -199,6 +201,27 @@ int seedmm_moe_ex(const int32_t *topk_ids, const float *topk_w, int T, int top_k
                   seedmm_mat gate, seedmm_mat up, seedmm_mat down,
                   void *workspace, size_t workspace_bytes, void *hip_stream,
                   const seedmm_side *side);
+
+/*
+ * seedmm_moe_noalloc -- seedmm_moe without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Its scratch memory is a static device array of the library,
+ * SEEDMM_NOALLOC_SCRATCH_BYTES (8 MiB) on every device it runs on, held until the process
+ * ends; the call allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine).  The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress) with the device current; make it outside graph capture.
+ *   Arguments, results and errors as seedmm_moe (one stream), plus SEEDMM_ESCRATCH when
+ *   seedmm_moe_workspace_bytes(T, top_k, E, H, I) exceeds SEEDMM_NOALLOC_SCRATCH_BYTES
+ *   (for 100 experts 2048 -> 1024 -> 2048, top-8: up to 96 tokens), checked before
+ *   anything runs.
+ *   Every call on one device shares that device's array: calls that overlap in time on
+ *   one device race (serialise them on one stream), and the array keeps the last call's
+ *   contents, which no call reads before writing them.
+ */
+#define SEEDMM_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int seedmm_moe_noalloc(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
+                       const void *x, float *y, int E, int H, int I, int P,
+                       seedmm_mat gate, seedmm_mat up, seedmm_mat down, void *hip_stream);
 
 /*
  * seedmm_moe_timed -- seedmm_moe that also records caller-created hipEvent_t handles on

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/seedmm.h"
 #include "moe_layer.hpp"
 #include "seed_decode.hpp"
@@ -1223,6 +1225,7 @@ const char* seedmm_strerror(int status) {
         case SEEDMM_EWORKSPACE: return "workspace missing or too small";
         case SEEDMM_EHIP: return "HIP launch failure";
         case SEEDMM_ECAPACITY: return "more distinct experts in one call than cache slots";
+        case SEEDMM_ESCRATCH: return "batch needs more scratch than the static buffer of seedmm_moe_noalloc";
         default: return "unknown status";
     }
 }
@@ -1481,3 +1484,53 @@ int seedmm_moe(const int32_t* topk_ids, const float* topk_w, int T, int top_k, c
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------------
+// seedmm_moe_noalloc: seedmm_moe with its workspace in a static device array.  Every
+// device the library runs on holds its own copy of `scratch` until the process ends.
+// In host code the array's name is only a stand-in: the device address of the current
+// device's copy comes from hipGetSymbolAddress, looked up once per device and kept.
+// ----------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = 8u << 20;   // SEEDMM_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == SEEDMM_NOALLOC_SCRATCH_BYTES, "header and library agree");
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once known
+
+// The current device's copy of `scratch` (nullptr if the lookup fails).
+void* scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int seedmm_moe_noalloc(const int32_t* topk_ids, const float* topk_w, int T,
+                                  int top_k, const void* x, float* y, int E, int H, int I,
+                                  int P, seedmm_mat gate, seedmm_mat up, seedmm_mat down,
+                                  void* hip_stream) {
+    if (P != 3 && P != 4) return SEEDMM_EINVAL;
+    const size_t need = seedmm_moe_workspace_bytes(T, top_k, E, H, I);
+    if (need == 0) return SEEDMM_EINVAL;
+    if (need > kScratchBytes) return SEEDMM_ESCRATCH;
+    if (T == 0) return SEEDMM_OK;
+    void* ws = scratch_of_current_device();
+    if (!ws) return SEEDMM_EHIP;
+    // Every scratch word the kernels read is written earlier in the same call (the
+    // dispatch writes all E counts and the lists up to them; the expert kernels write
+    // every SwiGLU row and per-slot output they later read), so nothing is cleared.
+    return moe_run(topk_ids, topk_w, T, top_k, x, y, E, H, I, P, nullptr, gate, up, down, ws,
+                   kScratchBytes, hip_stream, nullptr, nullptr, 0, nullptr);
+}

@@ -16,8 +16,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libseedmm.so")
 
-OK, EINVAL, EALIGN, EWORKSPACE, EHIP, ECAPACITY = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, EWORKSPACE, EHIP, ECAPACITY, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 8 << 20      # SEEDMM_NOALLOC_SCRATCH_BYTES of include/seedmm.h
 
 
 class SeedmmError(RuntimeError):
@@ -52,6 +53,8 @@ def _load():
     L.seedmm_moe.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, SeedMat, SeedMat, SeedMat,
                              p, ctypes.c_size_t, p]
     L.seedmm_moe_timed.argtypes = L.seedmm_moe.argtypes + [p]
+    L.seedmm_moe_noalloc.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, SeedMat, SeedMat,
+                                     SeedMat, p]
     L.seedmm_moe_ex.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, p, SeedMat, SeedMat,
                                 SeedMat, p, ctypes.c_size_t, p, ctypes.POINTER(SeedSide)]
     L.seedmm_search.argtypes = [p, i32, p, i32, i32, i32, ctypes.c_int32, p, p, p, p, p, p]
@@ -76,7 +79,8 @@ def _load():
     L.seedmm_strerror.argtypes = [i32]
     L.seedmm_version.restype = i32
     for name in ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
-                 "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_ex", "seedmm_search",
+                 "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_ex", "seedmm_moe_noalloc",
+                 "seedmm_search",
                  "seedmm_search_prepare", "seedmm_moe_mixed",
                  "seedmm_cache_init", "seedmm_cache_reset", "seedmm_cache_plan",
                  "seedmm_cache_moe", "seedmm_cache_stats"):
@@ -88,6 +92,7 @@ _lib = _load()
 
 EXPORTS = ("seedmm_gemv", "seedmm_gemv_ex", "seedmm_reconstruct", "seedmm_moe_dispatch",
            "seedmm_moe_workspace_bytes", "seedmm_moe", "seedmm_moe_timed", "seedmm_moe_ex",
+           "seedmm_moe_noalloc",
            "seedmm_moe_mixed", "seedmm_search", "seedmm_search_table_bytes",
            "seedmm_search_prepare", "seedmm_cache_record_layout", "seedmm_cache_state_bytes",
            "seedmm_cache_device_bytes",

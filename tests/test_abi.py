@@ -200,3 +200,16 @@ def test_binding_refuses_short_streams():
     with pytest.raises(ValueError, match="seeds"):
         seedmm._check_streams(t, E + 1, M, K, 3, "gate")
     seedmm._check_streams(t, E, M, K, 4, "gate", exact_coefs=False)   # mixed without Ps
+
+
+def test_noalloc_refuses_before_running(lib):
+    """seedmm_moe_noalloc checks the batch against its static scratch before it touches
+    the device: a batch needing more than 8 MiB is refused (no GPU needed)."""
+    from pseudo_random_weight_amd.seedmm import SeedMat, NOALLOC_SCRATCH_BYTES, ESCRATCH
+    m = SeedMat(FAKE, FAKE, FAKE, FAKE)
+    assert lib.seedmm_moe_workspace_bytes(128, 8, 100, 2048, 1024) > NOALLOC_SCRATCH_BYTES
+    f = lib.seedmm_moe_noalloc
+    assert f(FAKE, FAKE, 128, 8, FAKE, FAKE, 100, 2048, 1024, 4, m, m, m, None) == ESCRATCH
+    assert f(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 64, 64, 5, m, m, m, None) == -1    # P
+    assert f(FAKE, FAKE, 4, 0, FAKE, FAKE, 8, 64, 64, 4, m, m, m, None) == -1    # top_k
+    assert lib.seedmm_strerror(ESCRATCH) != lib.seedmm_strerror(99)
