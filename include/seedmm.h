@@ -184,7 +184,8 @@ int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,
  *   is a stream of hip_stream's device other than hip_stream, and side->fork and
  *   side->join are events (hipEventDisableTiming is enough), all created and owned by
  *   the caller.  Calls that may overlap in time must not share a seedmm_side.  One-token
- *   batches run on hip_stream alone (their kernels fill one wave round).
+ *   batches run on hip_stream alone (splitting their slots over two streams measured
+ *   slower: the cross-stream edges cost more than the overlap gains).
  * Errors: as seedmm_moe; SEEDMM_EINVAL also for P = 0 without p4mask, a p4mask with
  * P = 3 or 4, or a side stream given without both events or equal to hip_stream.  If the
  * fork cannot be recorded the call runs on hip_stream alone; if the join cannot be

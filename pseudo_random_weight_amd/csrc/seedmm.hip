@@ -355,6 +355,7 @@ __device__ __forceinline__ Window window_of(uint32_t seed16, const uint32_t* tab
 // zero weights.  The stream words of the next segment are loaded while the current one
 // is regenerated.  XL: the single token's activation row sits in LDS (xs, K bf16), so
 // the stream words are the loop's only global loads.
+
 template <int P, bool VEC, int NTA, int KS, bool TAB, bool XL = false>
 __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const* brow,
                                             f32x4* acc, const uint16_t* xs = nullptr) {
@@ -479,13 +480,11 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
 // 4 waves on 16 weight rows.  GATEUP: waves 0-1 regenerate gate, waves 2-3 up, each
 // over half of K; otherwise the 4 waves take a quarter of K each.
 // The products of one workgroup once its expert (e, n_e pairs in `list`) is known.
-template <int P, bool VEC, int NT, int MODE, bool TAB, int RT, bool XL = false>
-__device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, const int32_t* list,
-                                         const uint32_t* tab, f32x4 (*red)[NT][64],
-                                         const uint16_t* xs = nullptr) {
+// The lane state of wave `wave` of a workgroup serving expert e (row tile blockIdx.x).
+template <int P, int MODE, bool TAB, int RT>
+__device__ __forceinline__ Lane make_lane(const MfmaArgs& a, int e, const uint32_t* tab,
+                                          int wave, int lane, int& m0) {
     constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15;
     Lane L;
     L.tab = TAB ? tab : nullptr;
@@ -501,12 +500,24 @@ __device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, cons
     src.codes = second ? a.A2.codes : a.A.codes;
     src.exp_bias = second ? a.A2.exp_bias : a.A.exp_bias;
     L.W = mat_of(src, e, nblk, P, a.exp_bias, MODE != MODE_GEMM, a.p4mask, a.slot, a.slot_stride);
-    const int m0 = blockIdx.x * 16 * RT;
+    m0 = blockIdx.x * 16 * RT;
     const int row = m0 + 16 * (wave / KS % RT) + r;
     L.rv = row < a.M;
     L.rowb = (int64_t)(L.rv ? row : a.M - 1) * L.nbpr;
     L.nseg = (L.nbpr + 7) / 8;
     L.n_it = (L.nseg + KS * 4 - 1) / (KS * 4);
+    return L;
+}
+
+template <int P, bool VEC, int NT, int MODE, bool TAB, int RT, bool XL = false>
+__device__ __forceinline__ void mfma_run(const MfmaArgs& a, int e, int n_e, const int32_t* list,
+                                         const uint32_t* tab, f32x4 (*red)[NT][64],
+                                         const uint16_t* xs = nullptr) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int r = lane & 15;
+    int m0;
+    const Lane L = make_lane<P, MODE, TAB, RT>(a, e, tab, wave, lane, m0);
 
     if constexpr (NT == 1) {   // one token (n_e == 1)
         mfma_pass<P, VEC, 1, MODE, NT, TAB, RT, XL>(a, L, list, n_e, 0, m0, wave, lane, r, red, xs);
@@ -542,11 +553,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (P ==
     const int32_t* list = nullptr;
     if (MODE != MODE_GEMM && a.ids) {
         // one token: its top_k slots are top_k distinct experts, one workgroup row each
-        e = a.ids[blockIdx.y];
+        const int y = blockIdx.y;   // slot
+        e = a.ids[y];
         if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
         if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
         n_e = 1;
-        list = kSlotIota + blockIdx.y;
+        list = kSlotIota + y;
     } else if constexpr (MODE != MODE_GEMM) {
         // the target-th active expert (of this launch's P when the pack is mixed)
         const int target = blockIdx.y;
@@ -589,14 +601,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     extern __shared__ uint4 xs[];
     // the expert id, the activation row and the tables do not depend on each other: the
     // row's loads and the table fill run while the id is in flight
-    const int e = a.ids[blockIdx.y];
-    const int64_t row = MODE == MODE_GATEUP ? 0 : (int64_t)blockIdx.y;
+    const int y = blockIdx.y;   // slot
+    const int e = a.ids[y];
+    const int64_t row = MODE == MODE_GATEUP ? 0 : (int64_t)y;
     const uint4* src = (const uint4*)(a.x + row * a.ldx);
     for (int i = threadIdx.x; i < a.K / 8; i += 256) xs[i] = src[i];
     fill_lfsr_tables(tab);   // its barrier also publishes xs
     if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
     if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
-    mfma_run<P, VEC, 1, MODE, true, RT, true>(a, e, 1, kSlotIota + blockIdx.y, tab, red,
+    mfma_run<P, VEC, 1, MODE, true, RT, true>(a, e, 1, kSlotIota + y, tab, red,
                                               (const uint16_t*)xs);
 }
 
@@ -1049,7 +1062,9 @@ __global__ __launch_bounds__(256) void k_zero_rows(float* __restrict__ y, int ld
     y[(i / M) * ldy + i % M] = 0.0f;
 }
 
-// y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.
+// y[t][:] = sum_s o[t*top_k + s][:], slot order fixed.  KMAX > 0: top_k <= KMAX, and all
+// of a thread's slot loads are issued before the first add (the adds keep slot order).
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, int top_k,
                                                  float* __restrict__ y, int H, int T) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
@@ -1057,10 +1072,25 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o, in
     if (idx >= (int64_t)T * h4) return;
     const int64_t t = idx / h4, c = idx % h4;
     const float4* src = reinterpret_cast<const float4*>(o) + (t * top_k) * h4 + c;
-    float4 s = src[0];
-    for (int k = 1; k < top_k; ++k) {
-        const float4 v = src[(int64_t)k * h4];
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    float4 s;
+    if constexpr (KMAX > 0) {
+        float4 v[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (k < top_k) v[k] = src[(int64_t)k * h4];
+        s = v[0];
+#pragma unroll
+        for (int k = 1; k < KMAX; ++k) {
+            if (k < top_k) {
+                s.x += v[k].x; s.y += v[k].y; s.z += v[k].z; s.w += v[k].w;
+            }
+        }
+    } else {
+        s = src[0];
+        for (int k = 1; k < top_k; ++k) {
+            const float4 v = src[(int64_t)k * h4];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
     }
     reinterpret_cast<float4*>(y)[idx] = s;
 }
@@ -1436,8 +1466,11 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
 
     if (!direct) {
         const int64_t n4 = (int64_t)T * (H / 4);
-        hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                           obuf, top_k, y, H, T);
+        const dim3 cg((unsigned)((n4 + 255) / 256));
+        if (top_k <= 8)
+            hipLaunchKernelGGL(k_combine<8>, cg, dim3(256), 0, st, obuf, top_k, y, H, T);
+        else
+            hipLaunchKernelGGL(k_combine<0>, cg, dim3(256), 0, st, obuf, top_k, y, H, T);
     }
     mark(4);
     return launch_status();

@@ -384,14 +384,16 @@ def _raw_events(n):
     return out
 
 
-@pytest.mark.parametrize("E,P,T", [(8, 4, 600), (7, 3, 600), (12, 4, 16), (5, 3, 9)])
+@pytest.mark.parametrize("E,P,T", [(8, 4, 600), (7, 3, 600), (12, 4, 16), (5, 3, 9), (8, 4, 1),
+                                   (7, 3, 1)])
 def test_moe_prefill_two_streams(sm, oracle, E, P, T):
     """A layer call over several tokens with one P and a caller's side stream
     (seedmm_moe_ex) runs each half of the experts on its own stream, for the prefill
-    kernels (T = 600 here) and the decode ones (T = 16, 9).  Its output equals the
-    single-stream order of the timed call bit for bit (every expert served exactly once,
-    whatever the split point), matches the oracle, and graph replays of it reproduce the
-    eager result bit for bit."""
+    kernels (T = 600 here) and the decode ones (T = 16, 9); a single token runs on one
+    stream even when a side stream is given (T = 1).  Its output equals the single-stream
+    order of the timed call bit for bit (every expert served exactly once, whatever the
+    split point), matches the oracle, and graph replays of it reproduce the eager result
+    bit for bit."""
     import torch
     H, I, k = 256, 256, 2
     say("moe two streams", E, P, T)
