@@ -214,7 +214,8 @@ int seedmm_moe_ex(const int32_t *topk_ids, const float *topk_w, int T, int top_k
  *   Arguments, results and errors as seedmm_moe (one stream), plus SEEDMM_ESCRATCH when
  *   seedmm_moe_workspace_bytes(T, top_k, E, H, I) exceeds SEEDMM_NOALLOC_SCRATCH_BYTES
  *   (for 100 experts 2048 -> 1024 -> 2048, top-8: up to 96 tokens), checked before
- *   anything runs.
+ *   anything runs, and SEEDMM_EINVAL when hip_stream belongs to another device than the
+ *   current one (the array used is the current device's).
  *   Every call on one device shares that device's array: calls that overlap in time on
  *   one device race (serialise them on one stream), and the array keeps the last call's
  *   contents, which no call reads before writing them.

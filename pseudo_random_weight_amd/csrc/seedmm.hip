@@ -1535,10 +1535,9 @@ __device__ __align__(256) uint8_t scratch[kScratchBytes];
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once known
 
-// The current device's copy of `scratch` (nullptr if the lookup fails).
-void* scratch_of_current_device() {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+// Device `dev`'s copy of `scratch` (dev current; nullptr if the lookup fails).
+void* scratch_of_device(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
         void* p = nullptr;
@@ -1559,7 +1558,15 @@ extern "C" int seedmm_moe_noalloc(const int32_t* topk_ids, const float* topk_w, 
     if (need == 0) return SEEDMM_EINVAL;
     if (need > kScratchBytes) return SEEDMM_ESCRATCH;
     if (T == 0) return SEEDMM_OK;
-    void* ws = scratch_of_current_device();
+    // the array used is the current device's, so the stream must run on that device
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SEEDMM_EHIP;
+    if (hip_stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice((hipStream_t)hip_stream, &sdev) != hipSuccess || sdev != dev)
+            return SEEDMM_EINVAL;
+    }
+    void* ws = scratch_of_device(dev);
     if (!ws) return SEEDMM_EHIP;
     // Every scratch word the kernels read is written earlier in the same call (the
     // dispatch writes all E counts and the lists up to them; the expert kernels write
