@@ -388,14 +388,15 @@ def search_table(P: int, device=None, stream=None):
         n = int(_lib.seedmm_search_table_bytes(P))
         if n == 0:
             raise SeedmmError(EINVAL, "seedmm_search_table_bytes")
-        with _on(stream):
-            buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
-        off = (-buf.data_ptr()) % 256
-        tab = buf[off:off + n]
-        _check(_lib.seedmm_search_prepare(P, _ptr(tab), n, _stream(stream)),
-               "seedmm_search_prepare")
-        # later searches may run on other streams: wait for the fill once, here
-        (stream or torch.cuda.current_stream()).synchronize()
+        with torch.cuda.device(dev):   # the fill runs on that device (its current stream if none given)
+            with _on(stream):
+                buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+            off = (-buf.data_ptr()) % 256
+            tab = buf[off:off + n]
+            _check(_lib.seedmm_search_prepare(P, _ptr(tab), n, _stream(stream)),
+                   "seedmm_search_prepare")
+            # later searches may run on other streams: wait for the fill once, here
+            (stream or torch.cuda.current_stream()).synchronize()
         _TABLES[key] = (buf, tab)
     return _TABLES[key][1]
 
