@@ -35,6 +35,12 @@ sys.path.insert(0, ROOT)
 METRIC = "effective weights/s + compressed HBM GB/s (% roofline); MoE-layer decode tok/s"
 HBM_PEAK = 8.0e12                 # bytes/s, MI355X HBM3E
 VALU_PEAK = 256 * 4 * 16 * 2.4e9  # lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+
+
+def ALG_OPS(P):
+    """Algorithmic vector lane-ops per regenerated weight: P register states, P integer
+    multiply-adds c * (s - 32768), and one power-of-two scale per block of 8 weights."""
+    return 2 * P + 1.0 / 8
 MFMA_PEAK = 2.5e15                 # flop/s, dense bf16 matrix cores
 E, H, I, TOPK = 100, 2048, 1024, 8
 
@@ -615,7 +621,7 @@ def main():
     # dominant kernel: fused gate/up (two thirds of the weights)
     t_gu = stages[1]
     gu_weights = distinct.mean() * 2 * w_per_mat
-    alg_ops = gu_weights * (2 * P + 1)       # P states + P integer MACs + 1 scale per weight
+    alg_ops = gu_weights * ALG_OPS(P)
     traffic = read_traffic("gateup_T%d_P%d" % (T, P))
     traffic_note = ("calibrated FETCH_SIZE + WRITE_SIZE per launch read from "
                     "profiles/hbm_traffic.txt (rocprofv3 counter runs of the same kernel "
@@ -635,7 +641,7 @@ def main():
                     "unit": "lane-op/s", "frac": alg_ops / t_gu / VALU_PEAK,
                     "traffic": traffic, "traffic_source": traffic_note,
                     "kernel": "k_mfma<GATEUP> (fused gate/up + SwiGLU)",
-                    "alg_ops_per_weight": 2 * P + 1,
+                    "alg_ops_per_weight": ALG_OPS(P),
                     "kernel_us": t_gu * 1e6,
                     "compressed_bytes_per_launch": distinct.mean() * 2 * compressed_bytes_per_matrix(P),
                     "hbm_frac_compressed": distinct.mean() * 2 * compressed_bytes_per_matrix(P)
@@ -681,7 +687,7 @@ def main():
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
                               "gate_up_us": st[1] * 1e6, "down_us": st[2] * 1e6,
                               # event timing: includes a few microseconds of event records
-                              "gate_up_valu_frac": dis.mean() * 2 * w_per_mat * (2 * P + 1)
+                              "gate_up_valu_frac": dis.mean() * 2 * w_per_mat * ALG_OPS(P)
                               / st[1] / VALU_PEAK}
         out["by_batch"] = sweep
         if "1" in sweep:
