@@ -293,12 +293,34 @@ def _check_layer(T, k, topk_w, x, E, H, I, Ps, gate, up, down, exact_coefs=True)
         _check_streams(m, E, M, K, Ps, name, exact_coefs)
 
 
+def check_topk_ids(topk_ids, E: int):
+    """Host check of a routing's expert ids, which the layer calls leave to the caller:
+    every id in [0, E) and the top_k ids of each token distinct.  Copies the ids to the
+    host (a synchronisation); raises ValueError naming the first token that breaks it."""
+    ids = topk_ids.detach().to("cpu").to(torch.int64)
+    if ids.dim() != 2:
+        raise ValueError("topk_ids must be [T][top_k]")
+    bad = ((ids < 0) | (ids >= E)).any(dim=1)
+    if bool(bad.any()):
+        t = int(bad.nonzero()[0, 0])
+        raise ValueError(f"topk_ids[{t}] holds an expert id outside [0, {E})")
+    if ids.shape[1] > 1:
+        srt = ids.sort(dim=1).values
+        dup = (srt[:, 1:] == srt[:, :-1]).any(dim=1)
+        if bool(dup.any()):
+            t = int(dup.nonzero()[0, 0])
+            raise ValueError(f"topk_ids[{t}] names one expert twice")
+
+
 def moe(topk_ids, topk_w, x, E, H, I, P, gate, up, down, y=None, workspace=None, stream=None,
-        events=None, side=None):
+        events=None, side=None, check_ids=False):
     """Routed SwiGLU MoE layer (seedmm_moe); x bf16 [T][H] -> y fp32 [T][H].
     `events`: optional 5 raw hipEvent_t handles (ints) recorded between the stages
     (seedmm_moe_timed).  `side`: optional SideStream for the second half of the expert
-    launches (seedmm_moe_ex)."""
+    launches (seedmm_moe_ex).  `check_ids`: validate topk_ids on the host first
+    (check_topk_ids)."""
+    if check_ids:
+        check_topk_ids(topk_ids, E)
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")
@@ -343,11 +365,14 @@ def p4_mask(Ps, device) -> torch.Tensor:
 
 
 def moe_mixed(topk_ids, topk_w, x, E, H, I, p4mask, gate, up, down, y=None, workspace=None,
-              stream=None, Ps=None, side=None):
+              stream=None, Ps=None, side=None, check_ids=False):
     """Routed SwiGLU MoE layer with P chosen per expert (seedmm_moe_mixed); p4mask from
     p4_mask(Ps).  Given Ps, the coefficient streams are checked against it; without, only
     the seed and code streams are (the mask lives on the device).  `side`: optional
-    SideStream for the P = 3 launches (seedmm_moe_ex with P = 0)."""
+    SideStream for the P = 3 launches (seedmm_moe_ex with P = 0).  `check_ids`: validate
+    topk_ids on the host first (check_topk_ids)."""
+    if check_ids:
+        check_topk_ids(topk_ids, E)
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(x, torch.bfloat16, "x")

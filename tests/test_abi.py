@@ -213,3 +213,19 @@ def test_noalloc_refuses_before_running(lib):
     assert f(FAKE, FAKE, 4, 2, FAKE, FAKE, 8, 64, 64, 5, m, m, m, None) == -1    # P
     assert f(FAKE, FAKE, 4, 0, FAKE, FAKE, 8, 64, 64, 4, m, m, m, None) == -1    # top_k
     assert lib.seedmm_strerror(ESCRATCH) != lib.seedmm_strerror(99)
+
+
+def test_binding_checks_topk_ids_on_the_host():
+    """check_topk_ids (and moe's check_ids=True) refuses ids outside [0, E) and an expert
+    named twice by one token, naming the token; valid routings pass."""
+    import torch
+    from pseudo_random_weight_amd import seedmm
+    ok = torch.tensor([[0, 3, 7], [7, 1, 2]], dtype=torch.int32)
+    seedmm.check_topk_ids(ok, 8)
+    seedmm.check_topk_ids(torch.tensor([[5]], dtype=torch.int32), 8)
+    for bad, what in (([[0, 3, 8], [1, 2, 4]], "topk_ids[0]"), ([[0, 1, 2], [-1, 2, 3]], "topk_ids[1]"),
+                      ([[0, 1, 2], [4, 5, 4]], "topk_ids[1]")):
+        with pytest.raises(ValueError, match=re.escape(what)):
+            seedmm.check_topk_ids(torch.tensor(bad, dtype=torch.int32), 8)
+    with pytest.raises(ValueError):
+        seedmm.check_topk_ids(torch.tensor([1, 2], dtype=torch.int32), 8)
