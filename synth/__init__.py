@@ -117,12 +117,15 @@ def plant_degenerate(mat: dict, P: int, base: int, tag: str, frac: float = 0.02)
     return out
 
 
-def seed_matrix_mixed(base: int, tag: str, M: int, K: int, Ps, exp_bias: int = -4):
+def seed_matrix_mixed(base: int, tag: str, M: int, K: int, Ps, exp_bias=-4):
     """Random streams for len(Ps) stacked [M][K] matrices, matrix e with Ps[e] coefficients
     per block: each matrix generated on its own sub-stream, the streams concatenated in
-    matrix order (requires (M*K/8) % 4 == 0).  Also returns 'P' (int32[E])."""
+    matrix order (requires (M*K/8) % 4 == 0).  exp_bias: one value for every matrix or a
+    sequence of len(Ps).  Also returns 'P' (int32[E])."""
     assert (M * (K // 8)) % 4 == 0
-    parts = [seed_matrix(base, f"{tag}.m{e}", M, K, int(P), 1, exp_bias) for e, P in enumerate(Ps)]
+    eb = np.asarray(exp_bias, dtype=np.int64)
+    ebs = [int(eb)] * len(Ps) if eb.ndim == 0 else [int(v) for v in eb.reshape(len(Ps))]
+    parts = [seed_matrix(base, f"{tag}.m{e}", M, K, int(P), 1, ebs[e]) for e, P in enumerate(Ps)]
     out = {k: np.concatenate([p_[k] for p_ in parts]) for k in ("seeds", "coefs", "codes", "exp_bias")}
     out["P"] = np.asarray(Ps, dtype=np.int32)
     return out

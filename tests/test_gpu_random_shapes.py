@@ -112,3 +112,37 @@ def test_random_moe_matches_oracle(oracle, i):
     ref = oracle.moe(ids, w, x32, E, H, I, P, *mats)
     for t in range(T):
         assert rel_l2(y[t], ref[t]) <= 1e-2, t
+
+
+N_MIX = 8
+X_E = _draw("x.E", N_MIX, 2, 16)
+X_H = [8 * v for v in _draw("x.H8", N_MIX, 2, 40)]
+X_I = [8 * v for v in _draw("x.I8", N_MIX, 2, 40)]
+X_K = _draw("x.k", N_MIX, 1, 8)
+_XT, _XTP = _draw("x.T", N_MIX, 2, 100), _draw("x.TP", N_MIX, 300, 500)
+X_T = [(1, _XT[i], _XTP[i], _XT[i])[i % 4] for i in range(N_MIX)]   # one token, decode, prefill
+
+
+@pytest.mark.parametrize("i", range(N_MIX))
+def test_random_mixed_pack_matches_oracle(oracle, i):
+    """Mixed packs (P drawn per expert), per-expert biases in SiLU's curved range."""
+    import torch
+    from pseudo_random_weight_amd import seedmm as sm
+    E, H, I, T = X_E[i], X_H[i], X_I[i], X_T[i]
+    k = min(X_K[i], E)
+    Ps = [int(p) for p in synth.uniform_ints(BASE, f"x{i}.P", E, 3, 4)]
+    say("random mixed", i, E, H, I, k, T, "".join(map(str, Ps)))
+    mats = [synth.seed_matrix_mixed(BASE, f"x{i}.{n}", *((I, H) if n != "down" else (H, I)), Ps,
+                                    exp_bias=synth.uniform_ints(BASE, f"x{i}.{n}.eb", E, lo, lo + 2))
+            for n, lo in (("gate", -22), ("up", -21), ("down", -20))]
+    ids, w = synth.route_topk(BASE, f"x{i}.r", T, E, k)
+    bits = synth.bf16_bits(synth.normal_f32(BASE, f"x{i}.x", (T, H)))
+    x32 = synth.bf16_bits_to_f32(bits)
+    xt = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    y = sm.moe_mixed(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), xt, E, H, I,
+                     sm.p4_mask(Ps, "cuda"), *[_dev(m) for m in mats], Ps=Ps)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref = oracle.moe_mixed(ids, w, x32, E, H, I, Ps, *mats)
+    for t in range(T):
+        assert rel_l2(y[t], ref[t]) <= 1e-2, t
