@@ -206,7 +206,9 @@ def _check_numel(t, n, name):
 
 
 def gemv(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor = None):
-    """y = W x for fp32 x[K] (seedmm_gemv, default stream)."""
+    """y = W x for fp32 x[K] (seedmm_gemv).  The C call has no stream argument and runs on
+    the null stream; under another current stream the binding orders it after that
+    stream's earlier work and that stream's later work after it (events, no host wait)."""
     _mat(mat)
     _check_streams(mat, 1, M, K, P, "W")
     _dev(x, torch.float32, "x")
@@ -216,8 +218,16 @@ def gemv(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor = N
     _dev(y, torch.float32, "y")
     _check_numel(y, M, "y")
     eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
-    _check(_lib.seedmm_gemv(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb,
-                            _ptr(x), _ptr(y), M, K, P), "seedmm_gemv")
+    with torch.cuda.device(x.device):
+        cur, null = torch.cuda.current_stream(), torch.cuda.default_stream()
+        other = cur.cuda_stream != null.cuda_stream
+        if other:
+            null.wait_stream(cur)
+        status = _lib.seedmm_gemv(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]),
+                                  eb, _ptr(x), _ptr(y), M, K, P)
+        if other:
+            cur.wait_stream(null)
+    _check(status, "seedmm_gemv")
     return y
 
 
@@ -532,6 +542,8 @@ class ExpertCache:
         T, k = topk_ids.shape
         if ids_h.shape != (T, k):
             raise ValueError("topk_ids_host and topk_ids differ in shape")
+        _check_numel(topk_w, T * k, "topk_w")
+        _check_numel(x, T * self.H, "x")
         with _on(stream):
             if y is None:
                 y = torch.empty((T, self.H), dtype=torch.float32, device=x.device)
@@ -539,6 +551,7 @@ class ExpertCache:
                 workspace = torch.empty(moe_workspace_bytes(T, k, self.E, self.H, self.I),
                                         dtype=torch.uint8, device=x.device)
         _dev(y, torch.float32, "y")
+        _check_numel(y, T * self.H, "y")
         _check(_lib.seedmm_cache_moe(self.handle, ids_h.ctypes.data_as(ctypes.c_void_p),
                                      _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(x), _ptr(y),
                                      _ptr(workspace),

@@ -134,6 +134,28 @@ def test_cache_capacity_error_leaves_the_cache_usable(sm):
     assert np.array_equal(y.cpu().numpy(), y_ref.cpu().numpy())
 
 
+def test_cache_refuses_short_buffers_before_the_plan(sm):
+    """The binding checks y, x and topk_w against T before the call plans (and so
+    changes) the cache state."""
+    import torch
+    E, H, I, P, k, S = 8, 256, 128, 4, 2, 4
+    say("cache short buffers")
+    host = _layer(E, H, I, P, "csb")
+    cache = sm.ExpertCache(host, E, H, I, P, S)
+    ids = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    ids_d = torch.from_numpy(ids).cuda()
+    w = torch.full((2, 2), 0.5, dtype=torch.float32, device="cuda")
+    x = torch.randn(2, H).to(torch.bfloat16).cuda()
+    with pytest.raises(ValueError):
+        cache.moe(ids, ids_d, w, x, y=torch.empty((1, H), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        cache.moe(ids, ids_d, w, x[:1].contiguous())
+    with pytest.raises(ValueError):
+        cache.moe(ids, ids_d, w[:1].contiguous(), x)
+    assert cache.stats()["calls"] == 0
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("P", [4, 3])
 def test_cache_per_expert_biases_and_degenerate_blocks(sm, oracle, P):
     """Every expert's gate, up and down with an exp_bias of its own (gate outputs of order

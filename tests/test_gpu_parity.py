@@ -117,6 +117,31 @@ def test_gemv_one_hot_is_bit_exact(sm, oracle):
         np.testing.assert_array_equal(y.cpu().numpy(), Wref[:, k])
 
 
+def test_gemv_under_another_stream_waits_for_its_inputs(sm, oracle):
+    """seedmm_gemv runs on the null stream: under another current stream the binding orders
+    it after that stream's pending work.  x is written on the side stream behind a bounded
+    spin, and y is read back on that stream."""
+    import torch
+    say("gemv under a side stream")
+    M, K, P = 256, 512, 4
+    base = synth.config_seed(0)
+    mat = synth.seed_matrix(base, "gvside", M, K, P)
+    d = dev(mat)
+    x_host = synth.normal_f32(base, "xside", (K,))
+    src = torch.from_numpy(x_host).cuda()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        x = torch.zeros(K, dtype=torch.float32, device="cuda")
+        torch.cuda._sleep(2_000_000)           # a bounded spin that holds the stream back
+        x.copy_(src)
+        y = sm.gemv(d, x, M, K, P)
+        y2 = y * 1.0
+    side.synchronize()
+    ref = oracle.gemv(mat, x_host[None], M, K, P)[0]
+    assert rel_l2(y2.cpu().numpy(), ref) <= 1e-5
+
+
 @pytest.mark.parametrize("N", [2, 3, 5, 9])
 def test_gemv_ex_fp32_batches(sm, oracle, N):
     import torch
