@@ -126,14 +126,15 @@ int seedmm_reconstruct(const uint16_t *seeds, const uint16_t *coefs, const uint8
  *           increasing order, in lists[e*T .. e*T + counts[e]).  Entries past counts[e]
  *           are not written.
  * Deterministic.  Ids outside [0, E) are counted nowhere (the caller validates ids).
- * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k < 1, E < 1), SEEDMM_EHIP.
+ * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k < 1, E < 1, T*top_k >= 2^31),
+ * SEEDMM_EHIP.
  */
 int seedmm_moe_dispatch(const int32_t *topk_ids, int T, int top_k, int E, int32_t *counts,
                         int32_t *lists, void *hip_stream);
 
 /* Bytes of scratch memory seedmm_moe (and _ex, _timed, _mixed, seedmm_cache_moe) needs
  * for a batch of T tokens routed to top_k of E experts of hidden size H and intermediate
- * size I (0 on bad args): expert counts int32[E], pair lists int32[E][T], the SwiGLU rows
+ * size I (0 on bad args, T*top_k >= 2^31 among them): expert counts int32[E], pair lists int32[E][T], the SwiGLU rows
  * bf16 [T*top_k][I] and the per-slot outputs fp32 [T*top_k][H], each 256-byte aligned,
  * plus per-tile counts int32[ceil(T*top_k/8192)][E] above 8,192 pairs.  H and I enter
  * because the SwiGLU rows and the per-slot outputs dominate the size.  (Routed layer of
@@ -160,8 +161,8 @@ size_t seedmm_moe_workspace_bytes(int T, int top_k, int E, int H, int I);
  *   order, so results are bit-reproducible and a token's output does not depend on the
  *   other tokens of the batch.  All work runs on hip_stream (seedmm_moe_ex splits it
  *   over a second stream of the caller's).
- * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], E < 1 or
- * > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
+ * Errors: SEEDMM_EINVAL (null pointer, T < 0, top_k outside [1, min(E, 64)], T*top_k
+ * >= 2^31 (pair indices are int32), E < 1 or > 4096, H or I not a multiple of 8, P not 3/4, stacked streams not whole words),
  * SEEDMM_EALIGN (x not 16-byte aligned or H % 8 != 0), SEEDMM_EWORKSPACE, SEEDMM_EHIP.
  */
 int seedmm_moe(const int32_t *topk_ids, const float *topk_w, int T, int top_k,

@@ -1130,6 +1130,8 @@ void launch_gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int
                        y, ldy, M, K, N);
 }
 
+constexpr int kGridYMax = 65535;   // workgroup rows of one launch along y
+
 template <int P>
 void gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int eb, const float* x,
               int ldx, float* y, int ldy, int M, int K, int N, hipStream_t st) {
@@ -1137,9 +1139,16 @@ void gemv_f32(const uint16_t* s, const uint16_t* c, const uint8_t* d, int eb, co
     if (N <= 1) {
         if (vec) launch_gemv_f32<P, true, 1>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
         else launch_gemv_f32<P, false, 1>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
-    } else {
-        if (vec) launch_gemv_f32<P, true, 4>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
-        else launch_gemv_f32<P, false, 4>(s, c, d, eb, x, ldx, y, ldy, M, K, N, st);
+        return;
+    }
+    // 4 rows of X per workgroup row: larger N runs as several launches of whole chunks
+    constexpr int kChunk = kGridYMax * 4;
+    for (int n0 = 0; n0 < N; n0 += kChunk) {
+        const int n = N - n0 < kChunk ? N - n0 : kChunk;
+        const float* xc = x + (int64_t)n0 * ldx;
+        float* yc = y + (int64_t)n0 * ldy;
+        if (vec) launch_gemv_f32<P, true, 4>(s, c, d, eb, xc, ldx, yc, ldy, M, K, n, st);
+        else launch_gemv_f32<P, false, 4>(s, c, d, eb, xc, ldx, yc, ldy, M, K, n, st);
     }
 }
 
@@ -1228,8 +1237,12 @@ struct MoeLayout {
 
 int dispatch_tiles(int64_t pairs) { return (int)((pairs + kDispTile - 1) / kDispTile); }
 
+// Pair indices t * top_k + slot are int32 in the lists and the kernels.
+constexpr int64_t kMaxPairs = 0x7FFFFFFF;
+
 bool moe_layout(int T, int top_k, int E, int H, int I, MoeLayout* L) {
     if (T < 0 || top_k < 1 || E < 1 || H < 0 || I < 0) return false;
+    if ((int64_t)T * top_k > kMaxPairs) return false;
     const size_t pairs = (size_t)T * top_k;
     L->counts = 0;
     L->lists = L->counts + align_up(sizeof(int32_t) * (size_t)E);
@@ -1327,7 +1340,7 @@ int seedmm_reconstruct(const uint16_t* seeds, const uint16_t* coefs, const uint8
 
 int seedmm_moe_dispatch(const int32_t* topk_ids, int T, int top_k, int E, int32_t* counts,
                         int32_t* lists, void* hip_stream) {
-    if (T < 0 || top_k < 1 || E < 1) return SEEDMM_EINVAL;
+    if (T < 0 || top_k < 1 || E < 1 || (int64_t)T * top_k > kMaxPairs) return SEEDMM_EINVAL;
     if (!counts || !lists || (T > 0 && !topk_ids)) return SEEDMM_EINVAL;
     hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(256), 0, (hipStream_t)hip_stream, topk_ids,
                        T * top_k, T, counts, lists);
@@ -1350,6 +1363,7 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
             void* hip_stream, void* const* events, const int32_t* slot, int64_t slot_stride,
             const seedmm_side* side) {
     if (T < 0 || E < 1 || E > 4096 || top_k < 1 || top_k > E || top_k > 64) return SEEDMM_EINVAL;
+    if ((int64_t)T * top_k > kMaxPairs) return SEEDMM_EINVAL;
     if (H <= 0 || I <= 0 || H % 8 != 0 || I % 8 != 0) return SEEDMM_EINVAL;
     if (P == 0 ? !p4mask : (P != 3 && P != 4)) return SEEDMM_EINVAL;
     const int64_t nblk = (int64_t)I * (H / 8);   // blocks of one gate/up/down matrix
@@ -1361,7 +1375,7 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     if (!topk_ids || !topk_w || !x || !y) return SEEDMM_EINVAL;
     if (!aligned16(x) || !aligned16(y)) return SEEDMM_EALIGN;
     MoeLayout L;
-    moe_layout(T, top_k, E, H, I, &L);
+    if (!moe_layout(T, top_k, E, H, I, &L)) return SEEDMM_EINVAL;
     if (!workspace || workspace_bytes < L.total) return SEEDMM_EWORKSPACE;
     if (!aligned16(workspace)) return SEEDMM_EALIGN;
     hipStream_t st = (hipStream_t)hip_stream;

@@ -112,9 +112,21 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# raw handle of a device's current stream without building a torch Stream object
+_raw_current = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream_handle(index=None) -> int:
+    if index is None:
+        index = torch.cuda.current_device()
+    if _raw_current is not None:
+        return _raw_current(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
 def _stream(stream=None):
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(_current_stream_handle())
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -218,14 +230,16 @@ def gemv(mat: dict, x: torch.Tensor, M: int, K: int, P: int, y: torch.Tensor = N
     _dev(y, torch.float32, "y")
     _check_numel(y, M, "y")
     eb = int(mat["exp_bias_host"][0]) if "exp_bias_host" in mat else int(mat["exp_bias"][0])
-    with torch.cuda.device(x.device):
-        cur, null = torch.cuda.current_stream(), torch.cuda.default_stream()
-        other = cur.cuda_stream != null.cuda_stream
-        if other:
+    args = (_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]), eb, _ptr(x), _ptr(y),
+            M, K, P)
+    idx = x.device.index
+    if idx == torch.cuda.current_device() and _current_stream_handle(idx) == 0:
+        status = _lib.seedmm_gemv(*args)       # torch's default stream is the null stream
+    else:
+        with torch.cuda.device(x.device):
+            cur, null = torch.cuda.current_stream(), torch.cuda.default_stream()
             null.wait_stream(cur)
-        status = _lib.seedmm_gemv(_ptr(mat["seeds"]), _ptr(mat["coefs"]), _ptr(mat["codes"]),
-                                  eb, _ptr(x), _ptr(y), M, K, P)
-        if other:
+            status = _lib.seedmm_gemv(*args)
             cur.wait_stream(null)
     _check(status, "seedmm_gemv")
     return y

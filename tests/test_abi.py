@@ -104,12 +104,17 @@ def test_moe_rejects_and_workspace(lib):
     assert f(*args(wsb=16)) == -3            # workspace too small
     assert f(*args(x=FAKE + 2)) == -2        # x misaligned
     assert f(*args(T=0)) == 0                # empty batch: no-op
+    # pair indices t * top_k + slot are int32: 2^31 pairs or more are refused
+    assert lib.seedmm_moe_workspace_bytes(1 << 25, 64, 100, 8, 8) == 0
+    assert lib.seedmm_moe_workspace_bytes((1 << 25) - 1, 64, 100, 8, 8) > 0
+    assert f(*args(T=1 << 25, k=64, E=100, H=8, I=8, wsb=1 << 62)) == -1
 
 
 def test_dispatch_rejects(lib):
     assert lib.seedmm_moe_dispatch(FAKE, 4, 0, 8, FAKE, FAKE, None) == -1
     assert lib.seedmm_moe_dispatch(FAKE, -1, 2, 8, FAKE, FAKE, None) == -1
     assert lib.seedmm_moe_dispatch(FAKE, 4, 2, 0, FAKE, FAKE, None) == -1
+    assert lib.seedmm_moe_dispatch(FAKE, 1 << 25, 64, 8, FAKE, FAKE, None) == -1
 
 
 def test_binding_has_no_fallback():

@@ -160,6 +160,29 @@ def test_gemv_ex_fp32_batches(sm, oracle, N):
     assert rel_l2(y2.cpu().numpy(), 2 * ref) <= 1e-5
 
 
+def test_gemv_ex_fp32_rows_beyond_one_launch(sm, oracle):
+    """fp32 products take 4 rows of X per workgroup row, and a launch holds at most 65,535
+    workgroup rows: N = 4 * 65535 + 5 runs as two launches.  Every row within 1e-5 of the
+    oracle, and the rows of the second launch bit-equal to the same rows in a call of
+    their own (a row's sums do not depend on the other rows)."""
+    import torch
+    M, K, P, N = 16, 64, 4, 4 * 65535 + 5
+    say("gemv_ex fp32 rows beyond one launch", N)
+    base = synth.config_seed(0)
+    mat = synth.seed_matrix(base, "gvbig", M, K, P)
+    x = synth.normal_f32(base, "xbig", (N, K))
+    d = dev(mat)
+    xt = torch.from_numpy(x).cuda()
+    y = sm.gemv_ex(d, xt, M, K, P)
+    tail = sm.gemv_ex(d, xt[N - 9:].contiguous(), M, K, P)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref = oracle.gemv(mat, x, M, K, P)
+    err = np.linalg.norm(y.astype(np.float64) - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert err.max() <= 1e-5, int(err.argmax())
+    np.testing.assert_array_equal(y[N - 9:].view(np.uint32), tail.cpu().numpy().view(np.uint32))
+
+
 @pytest.mark.parametrize("P", [4, 3])
 @pytest.mark.parametrize("N", [1, 8, 16, 17, 64, 65, 300])
 def test_gemv_ex_bf16_matches_oracle(sm, oracle, P, N):
