@@ -335,9 +335,11 @@ int seedmm_search_prepare(int P, void *table, size_t table_bytes, void *hip_stre
  *              e * record; read by host-to-device copies only;
  *   exp_bias   device int32[3][E]: the exp_bias of gate, up and down of every expert
  *              (stays resident).
- * Calls on one cache must not overlap (one host thread, one stream at a time); the
- * host pack must stay unchanged while the cache is in use (seedmm_cache_reset after
- * changing it).
+ * Calls on one cache must not overlap (one host thread at a time), and their device work
+ * must run in call order: a call's record copies can overwrite slots that the previous
+ * call's kernels still read, so pass one stream to every call on a cache, or make the
+ * new call's stream wait for the previous call's.  The host pack must stay unchanged
+ * while the cache is in use (seedmm_cache_reset after changing it).
  */
 typedef struct seedmm_cache seedmm_cache;
 

@@ -480,7 +480,9 @@ def search(W: torch.Tensor, P: int, exp_bias: int, colw: torch.Tensor = None, er
 
 class ExpertCache:
     """A layer whose routed experts live in pinned host memory, with S device slots for
-    the recently used ones (seedmm_cache_*).  host: {"gate", "up", "down"} -> dicts of
+    the recently used ones (seedmm_cache_*).  Calls must reach the device in call order:
+    use one stream for every call on a cache (a call's record copies can overwrite slots
+    the previous call still reads).  host: {"gate", "up", "down"} -> dicts of
     numpy streams (seeds, coefs, codes, exp_bias) stacked as for moe(); they are packed
     once into expert records in pinned host memory (offsets from
     seedmm_cache_record_layout), and the exp_bias arrays go to device memory."""
