@@ -363,12 +363,15 @@ def test_one_token_matches_its_batch_and_the_oracle(sm, oracle, E, H, I, P, k):
         assert rel_l2(y1[0], ref[0]) <= 1e-2, t
 
 
-def test_moe_graph_replays_match_eager(sm):
+@pytest.mark.parametrize("T", [1, 4])
+def test_moe_graph_replays_match_eager(sm, T):
     """The layer call captured in a HIP graph: every replay, with eager work and
-    synchronisations between replays, gives the eager result bit for bit."""
+    synchronisations between replays, gives the eager result bit for bit.  The workspace
+    is filled with 0xFF before each replay, so no replay may depend on its contents
+    (one token: the dispatch-free path; four tokens: the dispatch lists)."""
     import torch
-    E, H, I, P, k, T = 100, 2048, 1024, 4, 8, 4
-    say("moe graph replay")
+    E, H, I, P, k = 100, 2048, 1024, 4, 8
+    say("moe graph replay", T)
     gate, up, down, ids, w, x = moe_case(T, E, H, I, P, k, 2, "graph")
     y_ref, _ = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
     g, u, d = dev(gate), dev(up), dev(down)
