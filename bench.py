@@ -600,8 +600,12 @@ def main():
         torch.cuda.synchronize()
         per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
         distinct = np.array([len(np.unique(ids_h[s_ % NB])) for s_ in range(steps)], dtype=np.float64)
+        # the output of input set 0 (replica 0) from one more replay, for the oracle check
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        y0 = y.cpu().numpy()
         del graphs
-        return wall / steps, distinct, np.percentile(per, [10, 50, 90])
+        return wall / steps, distinct, np.percentile(per, [10, 50, 90]), y0
 
     # stage times and the roofline come from eager launches with HIP events around each
     # kernel; the step time is HIP-graph replays unless --eager.  The eager run gets 30
@@ -611,7 +615,7 @@ def main():
     if args.eager:
         t_step = t_eager
     else:
-        t_step, distinct, pct = run_graph(T, args.warmup, args.steps)
+        t_step, distinct, pct, y_graph0 = run_graph(T, args.warmup, args.steps)
     w_per_mat = H * I
     weights = distinct.mean() * 3 * w_per_mat
     cbytes = distinct.mean() * 3 * compressed_bytes_per_matrix(P)
@@ -668,7 +672,7 @@ def main():
         out["step_ms_p10_p50_p90"] = [float(v) for v in pct]
         # the same graphs over a single weight copy: part of the layer stays in the
         # 256 MB last-level cache between steps (labelled, not the headline)
-        t_hot, dis_hot, pct_hot = run_graph(T, args.warmup, args.steps, nrep=1)
+        t_hot, dis_hot, pct_hot, _ = run_graph(T, args.warmup, args.steps, nrep=1)
         out["hot_cache"] = {"ms_per_step": t_hot * 1e3,
                             "weights_per_s": dis_hot.mean() * 3 * w_per_mat / t_hot,
                             "step_ms_p10_p50_p90": [float(v) for v in pct_hot],
@@ -681,7 +685,7 @@ def main():
                 continue
             ts, st, dis, *_ = run(Ts, 3, 20)
             if not args.eager:
-                ts, dis, _ = run_graph(Ts, 3, 50)
+                ts, dis, _, _ = run_graph(Ts, 3, 50)
             sweep[str(Ts)] = {"ms_per_step": ts * 1e3, "tok_s": Ts / ts,
                               "weights_per_s": dis.mean() * 3 * w_per_mat / ts,
                               "compressed_GBps": dis.mean() * 3 * compressed_bytes_per_matrix(P) / ts / 1e9,
@@ -749,6 +753,19 @@ def main():
                               "sample": f"blocks of {n_tok1} tokens, one thread, median of "
                                         f"{len(runs1)} runs"},
             "host": host_cpu()}
+        if not args.eager:
+            # the timed configuration against the oracle: the first tokens of input set 0
+            # as the graph replays computed them (two streams, replica 0 = these weights)
+            ids_g, w_g = synth.route_topk(base, f"router.T{T}.s0", T, E, TOPK)
+            x_g = synth.bf16_bits_to_f32(synth.bf16_bits(synth.normal_f32(base, f"x.T{T}.s0", (T, H))))
+            npar = min(4, T)
+            ref = oracle.moe(ids_g[:npar], w_g[:npar], x_g[:npar], E, H, I, P,
+                             host["gate"], host["up"], host["down"])
+            errs = [float(np.linalg.norm(y_graph0[t].astype(np.float64) - ref[t]) /
+                          max(np.linalg.norm(ref[t]), 1e-300)) for t in range(npar)]
+            out["parity"] = {"tokens": npar, "max_rel_l2": max(errs), "tolerance": 1e-2,
+                             "ok": max(errs) <= 1e-2,
+                             "path": "graph replay of the timed step, input set 0, replica 0"}
     print(json.dumps(out), flush=True)
 
 
