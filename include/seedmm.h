@@ -282,8 +282,9 @@ int seedmm_moe_mixed(const int32_t *topk_ids, const float *topk_w, int T, int to
  *   read: seeds uint16[M*K/8], coefs uint16[ceil(M*K/8*P/4)], codes uint8[ceil(M*K/16)],
  *   err: float64[M*K/8] squared error of each block (may be NULL).  A block for which
  *   no seed gives a solvable system gets seed 0, zero coefficients and err = +inf.
- *   Pairs (block, seed) that provably cannot win are skipped (a least-squares bound
- *   with a safe margin); the result is the same as evaluating them all.
+ *   Pairs (block, seed) that provably cannot win are skipped (a least-squares bound and,
+ *   at P = 4, a bound of every code's error, each with a safe margin); the result is the
+ *   same as evaluating them all.
  *   table: without importances (colw NULL), device memory of at least
  *   seedmm_search_table_bytes(P) bytes, 256-byte aligned, filled for this P by
  *   seedmm_search_prepare on hip_stream or before it in stream order (a table filled for
@@ -302,8 +303,9 @@ int seedmm_search(const float *W, int ldw, const float *colw, int M, int K, int 
 /*
  * The encoder's per-seed table for one P (barnson.org post, "LFSR is free": the pages'
  * encoder and decoder precompute per-seed streams; here the search precomputes, once per
- * P, each seed's basis rows along the register's cycle and the Cholesky factor of its
- * normal matrix): about 10.7 MB (P = 4) or 8.7 MB (P = 3) of caller-owned device memory.
+ * P, each seed's basis rows along the register's cycle, its normal matrix, the matrix's
+ * Cholesky factor and a certified bound of its smallest eigenvalue): about 16.5 MB
+ * (P = 4) or 12.3 MB (P = 3) of caller-owned device memory.
  * seedmm_search_table_bytes returns the size (0 for P not 3/4).  seedmm_search_prepare
  * fills `table` on hip_stream with kernels only (no host wait; capturable).
  * Errors: SEEDMM_EINVAL (P not 3/4, NULL table, table_bytes too small), SEEDMM_EALIGN

@@ -382,12 +382,15 @@ constexpr int kCycle = 65535;                 // the register's period
 constexpr int kXLen = kCycle + 64;            // cycle positions stepped (past one period)
 
 // Factor record of the seed at cycle position t, in doubles: the strictly lower entries
-// of L row by row, 1 / L_jj, the usable flag and the seed (its bits in the low word).
+// of L row by row, 1 / L_jj, an upper bound of 1 / lambda_min(A) (0 unless the seed is
+// usable), and the seed (its bits in the low word, the usable flag in bit 32).
 template <int P> struct SeedRecord {
-    static constexpr int kL = 0, kD = P * (P - 1) / 2, kFlag = kD + P, kSeed = kFlag + 1;
+    static constexpr int kL = 0, kD = P * (P - 1) / 2, kLam = kD + P, kSeed = kLam + 1;
     static constexpr int kSize = P == 4 ? 12 : 8;
     static_assert(kSeed < kSize, "record layout");
 };
+__device__ __forceinline__ int rec_seed(double v) { return (int)(uint32_t)__double_as_longlong(v); }
+__device__ __forceinline__ bool rec_usable(double v) { return (__double_as_longlong(v) >> 32) & 1; }
 // X record at cycle position u: x_{u+iP} - 32768, i = 0..7 (one 64-byte line).
 constexpr int kXRecs = kCycle + 8;
 constexpr int kSteps = kCycle + 1;           // steps walked: the cycle, then seed 1 again
@@ -396,8 +399,11 @@ constexpr int kSteps = kCycle + 1;           // steps walked: the cycle, then se
 // the X records (double[kXRecs][8]) and the factor records (double[kSteps][kSize]),
 // each part starting on a 256-byte boundary.
 struct TableLayout {
-    size_t cycle, xrec, chol, total;
+    size_t cycle, xrec, chol, amat, total;
 };
+// A = U^T U of the seed at cycle position t, upper triangle row by row (exact integers),
+// then sqrt(trace A) rounded up.
+constexpr int amat_size(int P) { return P * (P + 1) / 2 + 1; }
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline TableLayout table_layout(int P) {
     TableLayout L;
@@ -405,7 +411,8 @@ inline TableLayout table_layout(int P) {
     L.xrec = al256(sizeof(uint32_t) * kXLen);
     L.chol = L.xrec + al256(sizeof(double) * 8 * (size_t)kXRecs);
     const int ks = P == 4 ? SeedRecord<4>::kSize : SeedRecord<3>::kSize;
-    L.total = L.chol + al256(sizeof(double) * (size_t)ks * kSteps);
+    L.amat = L.chol + al256(sizeof(double) * (size_t)ks * kSteps);
+    L.total = L.amat + al256(sizeof(double) * (size_t)amat_size(P) * kSteps);
     return L;
 }
 
@@ -424,7 +431,8 @@ __global__ void k_cycle(uint32_t* __restrict__ x) {
 template <int P>
 __global__ __launch_bounds__(256) void k_seed_tables(const uint32_t* __restrict__ x,
                                                      double* __restrict__ xrec,
-                                                     double* __restrict__ chol) {
+                                                     double* __restrict__ chol,
+                                                     double* __restrict__ amat) {
     using Rec = SeedRecord<P>;
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t < kXRecs) {
@@ -449,6 +457,18 @@ __global__ __launch_bounds__(256) void k_seed_tables(const uint32_t* __restrict_
             for (int i = 0; i < 8; ++i) a += U[i][j] * U[i][k];
             A[j][k] = a;
         }
+    {
+        double* ar = amat + (int64_t)t * amat_size(P);
+        int o = 0;
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+#pragma unroll
+            for (int k = j; k < P; ++k) ar[o++] = A[j][k];
+        double tr = 0.0;
+#pragma unroll
+        for (int j = 0; j < P; ++j) tr += A[j][j];
+        ar[o] = sqrt(tr) * (1.0 + 1e-12);
+    }
     double L[P][P];
     bool pd = true;
     double det = 1.0, trace = 0.0;
@@ -482,8 +502,42 @@ __global__ __launch_bounds__(256) void k_seed_tables(const uint32_t* __restrict_
     double tp = 1.0;
 #pragma unroll
     for (int j = 0; j < P; ++j) tp *= trace;
-    rec[Rec::kFlag] = (pd && tp <= 1e7 * det) ? 1.0 : 0.0;
-    rec[Rec::kSeed] = __longlong_as_double((long long)x[t]);
+    const bool usable = pd && tp <= 1e7 * det;
+    // A lower bound of lambda_min(A): bisection on mu with an LDL^T factorisation of
+    // A - mu I (all pivots positive: positive definite), then less 1e-12 trace(A), which
+    // covers the factorisation's backward error (~P^2 eps |A|) many times over.
+    double lam = 0.0;
+    if (usable) {
+        double lo = 0.0, hi = A[0][0];
+#pragma unroll
+        for (int j = 1; j < P; ++j) hi = fmin(hi, A[j][j]);
+#pragma unroll 1
+        for (int it = 0; it < 48; ++it) {
+            const double mu = 0.5 * (lo + hi);
+            double l[P][P], d[P];
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                double dj = A[j][j] - mu;
+#pragma unroll
+                for (int k = 0; k < j; ++k) dj -= l[j][k] * l[j][k] * d[k];
+                ok = ok && dj > 0.0;
+                d[j] = dj > 0.0 ? dj : 1.0;
+#pragma unroll
+                for (int i = j + 1; i < P; ++i) {
+                    double v = A[i][j];
+#pragma unroll
+                    for (int k = 0; k < j; ++k) v -= l[i][k] * l[j][k] * d[k];
+                    l[i][j] = v / d[j];
+                }
+            }
+            if (ok) lo = mu;
+            else hi = mu;
+        }
+        lam = fmax(0.0, lo - 1e-12 * trace);
+    }
+    rec[Rec::kLam] = lam > 0.0 ? (1.0 / lam) * (1.0 + 1e-12) : 0.0;
+    rec[Rec::kSeed] = __longlong_as_double((long long)x[t] | ((long long)usable << 32));
 #pragma unroll
     for (int k = Rec::kSeed + 1; k < Rec::kSize; ++k) rec[k] = 0.0;
 }
@@ -493,19 +547,31 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
                                                       int K, int exp_bias, int64_t nblk,
                                                       const double* __restrict__ xtab,
                                                       const double* __restrict__ ctab,
+                                                      const double* __restrict__ atab,
                                                       uint16_t* __restrict__ seeds,
                                                       uint16_t* __restrict__ coefs,
                                                       uint8_t* __restrict__ codes,
                                                       double* __restrict__ errs) {
 #pragma clang fp contract(off)
     using Rec = SeedRecord<P>;
-    constexpr int QCAP = 256;                 // wave queue ring
+    // P = 4: the pairs past the residual bound go through the code bound first (it cut the
+    // exact evaluations from 12% to 2.4% of the pairs and the search time by 8%); at P = 3
+    // only 6% of the pairs pass the residual bound and the exact systems are smaller, so
+    // they go straight to the exact definition (the code bound measured 3% slower there).
+    constexpr bool kCodeBound = P == 4;
+    constexpr int QCAP = kCodeBound ? 256 : 1;    // wave ring of pairs past the residual bound
+    constexpr int QCAP2 = kCodeBound ? 128 : 256; // wave ring of pairs for the exact definition
     __shared__ double wv[8][8][64];           // per wave: the weights of its 64 blocks
     __shared__ double e0v[8][64], bestv[8][64];
     __shared__ unsigned long long mbits[8][64];   // merge: per block, best error bits,
     __shared__ int mkey[8][64];                   // its key and its nibbles
     __shared__ uint32_t mnib[8][64];
-    __shared__ uint32_t qe[8][QCAP];          // queued pairs: seed | block lane << 16
+    __shared__ uint32_t qe[8][QCAP];          // pairs past the residual bound: t | lane << 16
+    __shared__ double qy[8][QCAP][P];         // ... and their substitution vectors y
+    __shared__ uint32_t qe2[8][QCAP2];        // pairs past the code bound: seed | lane << 16
+    __shared__ double wl1[8][64];             // sum of |w_i| of each block
+    __shared__ unsigned long long ubits[8][64];   // per block: an upper bound of its final best
+                                                  // error (bits), from candidates still queued
     __shared__ uint32_t res[512][2];          // per block: seed | code << 16, coefficient nibbles
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t b0 = (int64_t)blockIdx.x * 512;
@@ -531,6 +597,12 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
         e0 += dd * dd;
     }
     e0v[wave][lane] = e0;
+    {
+        double l1 = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) l1 += fabs(w[i]);
+        wl1[wave][lane] = l1;
+    }
     double best = __builtin_inf();            // this lane's block: best candidate so far
     int bkey = 0x7FFFFFFF;                    // seed * 16 + code
     uint32_t bnib = 0;
@@ -684,7 +756,9 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
     // key when the error went down), and that candidate writes its nibbles.  One wave's
     // LDS operations take effect in program order.
     int qh = 0, qn = 0;                       // ring head and length (wave-uniform)
+    int qh2 = 0, qn2 = 0;                     // the same for the code-bound ring
     mbits[wave][lane] = (unsigned long long)__double_as_longlong(best);
+    ubits[wave][lane] = (unsigned long long)__double_as_longlong(best);
     mkey[wave][lane] = bkey;
     mnib[wave][lane] = bnib;
     auto run_batch = [&](int n) {
@@ -693,7 +767,7 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
         uint32_t cn = 0;
         int blk = 0;
         if (lane < n) {
-            const uint32_t ent = qe[wave][(qh + lane) & (QCAP - 1)];
+            const uint32_t ent = qe2[wave][(qh2 + lane) & (QCAP2 - 1)];
             blk = (int)(ent >> 16);
             exact(blk, (int)(ent & 0xFFFFu), bestv[wave][blk], cb, ck, cn);
         }
@@ -713,8 +787,189 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
         bkey = mkey[wave][lane];
         bnib = mnib[wave][lane];
         bestv[wave][lane] = best;
+        qh2 = (qh2 + n) & (QCAP2 - 1);
+        qn2 -= n;
+    };
+
+    // Code bound of the queued pairs, n <= 64 of them from the ring head, lane t on pair
+    // t; those it cannot rule out go on to the exact definition (run_batch).  In exact
+    // arithmetic every code's error is R + d^T A d with d = alpha - 2^e c, for any c.
+    // Computed from the tables: Rlb <= R <= Rub as in the step's bound; 1 / ilam <=
+    // lambda_min(A) (the table's certified bound); alpha~ = L^-T y misses alpha, and the
+    // definition's own solution alpha_o, by at most del = 1e-6 |alpha~|_1 (backward-stable
+    // solves, kappa(A) <= 1e7 for usable seeds) plus the correlation's rounding times ilam.
+    // A code is ruled out when its bound times (1 - 1e-12) exceeds thr, the block's best
+    // or a queued candidate's upper bound; gap = thr (1 + 4e-12) - Rlb covers that factor.
+    // With amax = max_j |alpha~_j| in [2^g, 2^(g+1)):
+    //   - codes e_lo .. e_lo + 5 (2^e from 2^(g-3) to 2^(g+2)): out if
+    //     sum_j (dist(alpha~_j, 2^e {-8..7}) - del)_+^2 > gap ilam (R + lambda_min |d|^2,
+    //     valid for every c), or, when no alpha~_j / 2^e lies within 2 del / 2^e of a
+    //     rounding boundary (then the definition's candidate is c~ = clamp(rint(alpha~ /
+    //     2^e))), if d~^T A d~ (1 - 1e-6) > (eta + sqrt(gap))^2 with d~ = alpha~ - 2^e c~,
+    //     the exact integer A, and eta = sqrt(trace A) sqrt(P) del >= |d - d~|_A;
+    //   - codes below (2^e <= amax / 16): the largest coefficient misses by at least
+    //     amax / 2 - del;
+    //   - codes above (2^e > 4 amax): the candidate is 0, with error e0 exactly (ties stay).
+    // Pairs with a code left go on to the exact ring, and give their block an upper bound
+    // of their best clear candidate's error at once, (Rub + (|d~|_A + eta)^2) (1 + 1e-12),
+    // or e0: the block's final best cannot exceed it (the candidate is evaluated).
+    auto run_bound = [&](int n) {
+        bool surv = false;
+        uint32_t out = 0;
+        double ub = __builtin_inf();
+        int ublk = 0;
+        if (lane < n) {
+            const int slot = (qh + lane) & (QCAP - 1);
+            const uint32_t ent = qe[wave][slot];
+            const int t = (int)(ent & 0xFFFFu), blk = (int)(ent >> 16);
+            ublk = blk;
+            const double* rec = ctab + (int64_t)t * Rec::kSize;
+            double rr[Rec::kSize];
+#pragma unroll
+            for (int k = 0; k < Rec::kSize; ++k) rr[k] = rec[k];
+            out = (uint32_t)rec_seed(rr[Rec::kSeed]) | ((uint32_t)blk << 16);
+            const double e0l = e0v[wave][blk];
+            const double thr = fmin(bestv[wave][blk], __longlong_as_double((long long)ubits[wave][blk]));
+            const double ilam = rr[Rec::kLam];
+            surv = true;
+            if (rec_usable(rr[Rec::kSeed]) && e0l > 0.0 && thr < __builtin_inf() && ilam > 0.0) {
+                double y[P], al[P], q = 0.0;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    y[j] = qy[wave][slot][j];
+                    q = __builtin_fma(y[j], y[j], q);
+                }
+                const double Rlb = ((e0l - q) - 1e-6 * e0l) * (1.0 - 1e-12);
+                const double gap = thr * (1.0 + 4e-12) - Rlb;
+                surv = gap >= 0.0;   // else every code's error is at least R > thr
+                if (surv) {
+#pragma unroll
+                    for (int j = P - 1; j >= 0; --j) {
+                        double v = y[j];
+#pragma unroll
+                        for (int k = j + 1; k < P; ++k)
+                            v = __builtin_fma(-rr[Rec::kL + k * (k - 1) / 2 + j], al[k], v);
+                        al[j] = v * rr[Rec::kD + j];
+                    }
+                    constexpr int NA = amat_size(P);
+                    double am[NA];
+                    const double* arec = atab + (int64_t)t * NA;
+#pragma unroll
+                    for (int k = 0; k < NA; ++k) am[k] = arec[k];
+                    auto aidx = [](int j, int k) { return j * P - j * (j - 1) / 2 + (k - j); };   // j <= k
+                    double l1a = 0.0, amax = 0.0;
+#pragma unroll
+                    for (int j = 0; j < P; ++j) {
+                        l1a += fabs(al[j]);
+                        amax = fmax(amax, fabs(al[j]));
+                    }
+                    // the correlation c = U^T w was summed in double: |error| <= 8 eps 2^15
+                    // |w|_1 per component, which moves alpha by sqrt(P) that / lambda_min
+                    const double del = 1e-6 * l1a + 4.0 * (8.0 * 1.2e-16 * 32768.0) * wl1[wave][blk] * ilam;
+                    const double eta = am[NA - 1] * 2.0 * del;
+                    const double glam = gap * ilam * (1.0 + 1e-12);
+                    const double sg = sqrt(gap) * (1.0 + 1e-12) + eta;
+                    const double ath = sg * sg * (1.0 + 2e-6);
+                    // d~^T A d~ of one code's candidate
+                    auto qform = [&](const double* dd) {
+                        double qa = 0.0;
+#pragma unroll
+                        for (int j = 0; j < P; ++j) {
+                            double v = am[aidx(j, j)] * dd[j];
+#pragma unroll
+                            for (int k = j + 1; k < P; ++k) v = __builtin_fma(2.0 * am[aidx(j, k)], dd[k], v);
+                            qa = __builtin_fma(dd[j], v, qa);
+                        }
+                        return fmax(qa, 0.0);
+                    };
+                    bool open = amax == 0.0;   // alpha~ = 0: the bound is Rlb <= thr
+                    int elo = 0;
+                    if (!open) {
+                        elo = min(max(ilogb(amax) - 3 - exp_bias + 15, 0), 16);
+                        if (elo > 0) {
+                            const double d = fmax(0.5 * amax - del, 0.0);
+                            open = open || !(d * d > glam);
+                        }
+                        if (elo + 6 <= 15) open = open || !(e0l > thr);
+                        double sc = __builtin_ldexp(1.0, elo + exp_bias - 15);
+                        double inv = __builtin_ldexp(1.0, -(elo + exp_bias - 15));
+#pragma unroll
+                        for (int c = 0; c < 6; ++c) {
+                            if (elo + c <= 15) {
+                                const double tol = 2.0 * del * inv;
+                                double dd[P], s2 = 0.0;
+                                bool clear = true;
+#pragma unroll
+                                for (int j = 0; j < P; ++j) {
+                                    const double tj = al[j] * inv;
+                                    const double rj = __builtin_rint(tj);
+                                    clear = clear && (0.5 - fabs(tj - rj)) > tol;
+                                    dd[j] = __builtin_fma(-sc, fmin(fmax(rj, -8.0), 7.0), al[j]);
+                                    const double dj = fmax(fabs(dd[j]) - del, 0.0);
+                                    s2 = __builtin_fma(dj, dj, s2);
+                                }
+                                bool gone = s2 > glam;
+                                if (!gone && clear) gone = qform(dd) > ath;
+                                open = open || !gone;
+                            }
+                            sc *= 2.0;
+                            inv *= 0.5;
+                        }
+                    }
+                    surv = open;
+                    if (surv && amax > 0.0) {
+                        // the upper bound of this pair's best clear candidate (rare)
+                        const double Rub = ((e0l - q) + 1e-6 * e0l) * (1.0 + 1e-12);
+                        if (elo + 6 <= 15) ub = e0l;
+                        double sc = __builtin_ldexp(1.0, elo + exp_bias - 15);
+                        double inv = __builtin_ldexp(1.0, -(elo + exp_bias - 15));
+                        for (int c = 0; c < 6 && elo + c <= 15; ++c) {
+                            const double tol = 2.0 * del * inv;
+                            double dd[P];
+                            bool clear = true;
+#pragma unroll
+                            for (int j = 0; j < P; ++j) {
+                                const double tj = al[j] * inv;
+                                const double rj = __builtin_rint(tj);
+                                clear = clear && (0.5 - fabs(tj - rj)) > tol;
+                                dd[j] = __builtin_fma(-sc, fmin(fmax(rj, -8.0), 7.0), al[j]);
+                            }
+                            if (clear) {
+                                const double nup = sqrt(qform(dd) * (1.0 + 1e-6)) + eta;
+                                ub = fmin(ub, __builtin_fma(nup, nup, Rub) * (1.0 + 1e-12));
+                            }
+                            sc *= 2.0;
+                            inv *= 0.5;
+                        }
+                    }
+                }
+            }
+        }
+        const bool go = surv && lane < n;
+        // survivors lower their block's bound at once (non-negative doubles order like
+        // their bits); the exact ring still evaluates them against the true best
+        if (go && ub < __builtin_inf())
+            __hip_atomic_fetch_min(&ubits[wave][ublk], (unsigned long long)__double_as_longlong(ub),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint64_t bal = __ballot(go);
+        if (go) {
+            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+            qe2[wave][(qh2 + qn2 + __popcll(below)) & (QCAP2 - 1)] = out;
+        }
+        qn2 += __popcll(bal);
         qh = (qh + n) & (QCAP - 1);
         qn -= n;
+    };
+    // drain the residual-bound ring, keeping the exact ring below 64 + 64 entries
+    auto drain = [&]() {
+        if constexpr (kCodeBound) {
+            while (qn >= 64) {
+                run_bound(64);
+                while (qn2 >= 64) run_batch(64);
+            }
+        } else {
+            while (qn2 >= 64) run_batch(64);
+        }
     };
 
     // c_{t+1} .. c_{t+P} of the current cycle position t
@@ -727,7 +982,7 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
         cw[j] = acc;
     }
     // One step along the cycle from its records: bound, queue, slide the window.
-    auto step = [&](const double* rec, const double* xn) {
+    auto step = [&](const double* rec, const double* xn, int t) {
         // bound (fused multiply-adds are fine here: the margin covers any rounding)
         double y[P], q = 0.0;
         int o = Rec::kL;
@@ -740,17 +995,30 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
             y[j] = v * rec[Rec::kD + j];
             q = __builtin_fma(y[j], y[j], q);
         }
-        const int s = (int)(uint32_t)__double_as_longlong(rec[Rec::kSeed]);
+        const int s = rec_seed(rec[Rec::kSeed]);
         const double lb = ((e0 - q) - 1e-6 * e0) * (1.0 - 1e-12);
-        const bool prune = ((rec[Rec::kFlag] != 0.0) & (e0 > 0.0) & (best < __builtin_inf()) & (lb > best)) |
+        // the block's best so far, or the upper bound that a queued candidate already gives
+        const double thr = kCodeBound ? fmin(best, __longlong_as_double((long long)ubits[wave][lane])) : best;
+        const bool prune = (rec_usable(rec[Rec::kSeed]) & (e0 > 0.0) & (thr < __builtin_inf()) & (lb > thr)) |
                            ((best == 0.0) & (s * 16 > bkey));
         const bool keep = active & !prune;
         const uint64_t bal = __ballot(keep);
-        if (keep) {
-            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
-            qe[wave][(qh + qn + __popcll(below)) & (QCAP - 1)] = (uint32_t)s | ((uint32_t)lane << 16);
+        if constexpr (kCodeBound) {
+            if (keep) {
+                const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+                const int slot = (qh + qn + __popcll(below)) & (QCAP - 1);
+                qe[wave][slot] = (uint32_t)t | ((uint32_t)lane << 16);
+#pragma unroll
+                for (int j = 0; j < P; ++j) qy[wave][slot][j] = y[j];
+            }
+            qn += __popcll(bal);
+        } else {   // straight to the exact definition
+            if (keep) {
+                const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+                qe2[wave][(qh2 + qn2 + __popcll(below)) & (QCAP2 - 1)] = (uint32_t)s | ((uint32_t)lane << 16);
+            }
+            qn2 += __popcll(bal);
         }
-        qn += __popcll(bal);
         // slide the window: c_{t+P+1} in, c_{t+1} out
         double cn = 0.0;
 #pragma unroll
@@ -776,14 +1044,24 @@ __global__ __launch_bounds__(512) void k_search_lanes(const float* __restrict__ 
             xa[i] = pxa[i];
             xb[i] = pxa[8 + i];
         }
-        step(ra, xa);
-        step(rb, xb);
-        while (qn >= 64) run_batch(64);
+        step(ra, xa, t);
+        step(rb, xb, t + 1);
+        drain();
         // every 64 steps the group's waves meet, so they read the same table records
         // at about the same time and one wave's cache misses are the others' hits
         if ((t & 63) == 0) __syncthreads();
     }
-    if (qn > 0) run_batch(qn);
+    // the rest of both rings, one batch at a time
+#pragma unroll 1
+    while (qn > 0 || qn2 > 0) {
+        if constexpr (kCodeBound) {
+            if (qn > 0) {
+                run_bound(qn < 64 ? qn : 64);
+                continue;
+            }
+        }
+        run_batch(qn2 < 64 ? qn2 : 64);
+    }
 
     if (bkey != 0x7FFFFFFF) {
         res[threadIdx.x][0] = (uint32_t)(bkey >> 4) | ((uint32_t)(bkey & 15) << 16);
@@ -836,8 +1114,8 @@ extern "C" int seedmm_search_prepare(int P, void* table, size_t table_bytes, voi
     uint32_t* x = (uint32_t*)(base + L.cycle);
     hipLaunchKernelGGL(k_cycle, dim3(1), dim3(64), 0, st, x);
     const dim3 grid((kXRecs + 255) / 256);   // kXRecs >= kSteps
-    if (P == 4) hipLaunchKernelGGL(k_seed_tables<4>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)(base + L.xrec), (double*)(base + L.chol));
-    else hipLaunchKernelGGL(k_seed_tables<3>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)(base + L.xrec), (double*)(base + L.chol));
+    if (P == 4) hipLaunchKernelGGL(k_seed_tables<4>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)(base + L.xrec), (double*)(base + L.chol), (double*)(base + L.amat));
+    else hipLaunchKernelGGL(k_seed_tables<3>, grid, dim3(256), 0, st, (const uint32_t*)x, (double*)(base + L.xrec), (double*)(base + L.chol), (double*)(base + L.amat));
     return hipGetLastError() == hipSuccess ? SEEDMM_OK : SEEDMM_EHIP;
 }
 
@@ -859,9 +1137,10 @@ extern "C" int seedmm_search(const float* W, int ldw, const float* colw, int M, 
         const TableLayout L = table_layout(P);
         const double* xt = (const double*)((const char*)table + L.xrec);
         const double* ct = (const double*)((const char*)table + L.chol);
+        const double* at = (const double*)((const char*)table + L.amat);
         const dim3 grid((unsigned)((nblk + 511) / 512));
-        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
-        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, seeds, coefs, codes, err);
+        if (P == 4) hipLaunchKernelGGL((k_search_lanes<4>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, at, seeds, coefs, codes, err);
+        else hipLaunchKernelGGL((k_search_lanes<3>), grid, dim3(512), 0, st, W, (int64_t)ldw, K, exp_bias, nblk, xt, ct, at, seeds, coefs, codes, err);
     } else {
         const dim3 grid((unsigned)((nblk + 3) / 4));
         if (P == 4) hipLaunchKernelGGL((k_search<4, true>), grid, dim3(256), 0, st, W, (int64_t)ldw, colw, K, exp_bias, nblk, seeds, coefs, codes, err);
