@@ -356,20 +356,38 @@ __device__ __forceinline__ Window window_of(uint32_t seed16, const uint32_t* tab
 // is regenerated.  XL: the single token's activation row sits in LDS (xs, K bf16), so
 // the stream words are the loop's only global loads.
 
-template <int P, bool VEC, int NTA, int KS, bool TAB, bool XL = false>
+// Segment of iteration `it` of a lane (KS waves share one K range): its first block
+// gc * 8 (clamped into the row) and how many of its blocks exist.
+template <int KS>
+__device__ __forceinline__ void seg_of(const Lane& L, int it, int& gc, int& nvalid) {
+    const int g = it * (KS * 4) + L.ks * 4 + L.q;
+    gc = g < L.nseg ? g : L.nseg - 1;
+    nvalid = (g < L.nseg && L.rv) ? min(8, L.nbpr - gc * 8) : 0;
+}
+
+// The stream words of a lane's first segment.
+template <int P, bool VEC, int KS>
+__device__ __forceinline__ Seg<P, VEC> first_seg(const Lane& L) {
+    int gc, nvalid;
+    seg_of<KS>(L, 0, gc, nvalid);
+    Seg<P, VEC> s;
+    s.load(L.W.seeds, L.W.coefs, L.W.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
+    return s;
+}
+
+// PRE: the first segment's words were loaded by the caller (`pre`, from first_seg), so
+// their latency overlaps the caller's set-up.
+template <int P, bool VEC, int NTA, int KS, bool TAB, bool XL = false, bool PRE = false>
 __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const* brow,
-                                            f32x4* acc, const uint16_t* xs = nullptr) {
+                                            f32x4* acc, const uint16_t* xs = nullptr,
+                                            const Seg<P, VEC>* pre = nullptr) {
     static_assert(!XL || NTA == 1, "the LDS activation row serves one token");
-    constexpr int GSTRIDE = KS * 4;
-    auto seg = [&](int it, int& gc, int& nvalid) {
-        const int g = it * GSTRIDE + L.ks * 4 + L.q;
-        gc = g < L.nseg ? g : L.nseg - 1;
-        nvalid = (g < L.nseg && L.rv) ? min(8, L.nbpr - gc * 8) : 0;
-    };
+    auto seg = [&](int it, int& gc, int& nvalid) { seg_of<KS>(L, it, gc, nvalid); };
     int gc, nvalid;
     seg(0, gc, nvalid);
     Seg<P, VEC> cur;
-    cur.load(L.W.seeds, L.W.coefs, L.W.codes, L.rowb + gc * 8, VEC ? 8 : nvalid);
+    if constexpr (PRE) cur = *pre;
+    else cur = first_seg<P, VEC, KS>(L);
     for (int it = 0; it < L.n_it; ++it) {
         int gn, nvn;
         seg(it + 1 < L.n_it ? it + 1 : it, gn, nvn);
@@ -407,10 +425,12 @@ __device__ __forceinline__ void mfma_k_loop(const Lane& L, const uint16_t* const
 }
 
 // One pass: NTA tiles of 16 tokens starting at token slot `pass`.
-template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB, int RT, bool XL = false>
+template <int P, bool VEC, int NTA, int MODE, int NT, bool TAB, int RT, bool XL = false,
+          bool PRE = false>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, const int32_t* list,
                                           int n_e, int pass, int m0, int wave, int lane, int r,
-                                          f32x4 (*red)[NT][64], const uint16_t* xs = nullptr) {
+                                          f32x4 (*red)[NT][64], const uint16_t* xs = nullptr,
+                                          const Seg<P, VEC>* pre = nullptr) {
     constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;   // waves sharing one K range
     // B rows of this lane (token column r of every tile); slots past n_e repeat the last
     // token so every load stays in range -- their outputs are never stored.
@@ -427,7 +447,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs& a, const Lane& L, cons
     f32x4 acc[NTA];
 #pragma unroll
     for (int t = 0; t < NTA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_k_loop<P, VEC, NTA, KS, TAB, XL>(L, brow, acc, xs);
+    mfma_k_loop<P, VEC, NTA, KS, TAB, XL, PRE>(L, brow, acc, xs, pre);
 
     // partial sums of the four waves meet in LDS (fixed order); wave c % 4 finishes the
     // (row tile, token tile) pair c
@@ -596,21 +616,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (P ==
 template <int P, bool VEC, int MODE, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mfma_one(const MfmaArgs a) {
     static_assert(MODE != MODE_GEMM, "one-token kernel of the routed layer");
+    constexpr int KS = MODE == MODE_GATEUP ? 2 : 4 / RT;
     __shared__ f32x4 red[4][1][64];
     __shared__ uint32_t tab[512];
     extern __shared__ uint4 xs[];
-    // the expert id, the activation row and the tables do not depend on each other: the
-    // row's loads and the table fill run while the id is in flight
+    // Start-up: the activation row's first piece and the first segment's stream words
+    // are requested together, before the tables are computed and the barrier, so the
+    // two memory latencies overlap each other and the table fill.
     const int y = blockIdx.y;   // slot
     const int e = a.ids[y];
+    const int tid = threadIdx.x;
     const int64_t row = MODE == MODE_GATEUP ? 0 : (int64_t)y;
     const uint4* src = (const uint4*)(a.x + row * a.ldx);
-    for (int i = threadIdx.x; i < a.K / 8; i += 256) xs[i] = src[i];
-    fill_lfsr_tables(tab);   // its barrier also publishes xs
-    if (e < 0 || e >= a.E) return;   // uniform; invalid ids are the caller's error
-    if (a.p4mask && p4_of(a.p4mask, e) != (P == 4)) return;   // the other launch's
-    mfma_run<P, VEC, 1, MODE, true, RT, true>(a, e, 1, kSlotIota + y, tab, red,
-                                              (const uint16_t*)xs);
+    const int nx = a.K / 8;
+    uint4 x0 = {0u, 0u, 0u, 0u};
+    if (tid < nx) x0 = src[tid];
+    // uniform; invalid ids are the caller's error, other-P experts the other launch's
+    const bool serve = e >= 0 && e < a.E && !(a.p4mask && p4_of(a.p4mask, e) != (P == 4));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    int m0 = 0;
+    Lane L;
+    Seg<P, VEC> first;
+    if (serve) {
+        L = make_lane<P, MODE, true, RT>(a, e, tab, wave, lane, m0);
+        first = first_seg<P, VEC, KS>(L);
+    }
+    for (int i = tid; i < 512; i += 256)
+        tab[i] = lfsr_next32(i < 256 ? (uint32_t)i : (uint32_t)(i - 256) << 8);
+    if (tid < nx) xs[tid] = x0;
+    for (int i = tid + 256; i < nx; i += 256) xs[i] = src[i];
+    __syncthreads();   // publishes the tables and xs
+    if (!serve) return;
+    mfma_pass<P, VEC, 1, MODE, 1, true, RT, true, true>(a, L, kSlotIota + y, 1, 0, m0, wave,
+                                                        lane, lane & 15, red,
+                                                        (const uint16_t*)xs, &first);
 }
 
 // ----------------------------------------------------------------------------------
