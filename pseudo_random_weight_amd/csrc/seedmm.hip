@@ -653,6 +653,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                         (const uint16_t*)xs, &first);
 }
 
+// One token, down with the combine folded in: a workgroup owns 8 rows of y for all top_k
+// (<= 8) slots, so the slot outputs meet in its LDS and no other launch adds them.
+// Wave w regenerates rows m0..m0+7 of the down matrices of slots 2(w/2) and 2(w/2)+1
+// (A rows 0-7 and 8-15) over K half w % 2, which is the K split, segment order and MFMA
+// sequence of k_mfma_one's down for every row.  The activation rows (the slots' h rows)
+// sit in LDS; B column n is slot n's row, so D[(slot s, row), s] is that row's product.
+// The epilogue forms each slot's output as k_mfma_one does (the two K halves, then the
+// router weight) and adds them in slot order from slot 0, as k_combine does, so y is bit
+// for bit the three-launch result.  Lanes of a missing slot (s >= top_k) or an invalid
+// id regenerate zero weights and their slots are not added.  Dynamic LDS: top_k K bf16.
+template <int P, bool VEC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_down_one(const MfmaArgs a) {
+    constexpr int KS = 2;
+    __shared__ f32x4 red[8][64];
+    __shared__ uint32_t tab[512];
+    extern __shared__ uint4 xs[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int r = lane & 15;
+    const int kk = a.top_k;
+    const int slot = 2 * (wave >> 1) + (r >> 3);   // this lane's A row: slot, row m0 + (r & 7)
+    const int m0 = blockIdx.x * 8;
+    const int nk = a.K / 8;                        // 16-byte pieces of one h row
+    const int np = kk * nk;                        // h rows of the slots are consecutive
+    const uint4* src = (const uint4*)a.x;
+    uint4 x0 = {0u, 0u, 0u, 0u};
+    if (tid < np) x0 = src[tid];
+    const int e = slot < kk ? a.ids[slot] : -1;
+    const bool serve = e >= 0 && e < a.E;
+    Lane L;
+    L.tab = tab;
+    L.ks = wave % KS;
+    L.q = lane >> 4;
+    L.nbpr = nk;
+    const int64_t nblk = (int64_t)a.M * L.nbpr;
+    // a lane without an expert reads expert 0's stacked streams (or cache slot 0's, which
+    // is where the stream pointers point): in range, and its weights are zeroed anyway
+    L.W = serve ? mat_of(a.A, e, nblk, P, 0, true, nullptr, a.slot, a.slot_stride)
+                : mat_of(a.A, 0, nblk, P, 0, true);
+    const int row = m0 + (r & 7);
+    L.rv = serve && row < a.M;
+    L.rowb = (int64_t)(row < a.M ? row : a.M - 1) * L.nbpr;
+    L.nseg = (L.nbpr + 7) / 8;
+    L.n_it = (L.nseg + KS * 4 - 1) / (KS * 4);
+    const Seg<P, VEC> first = first_seg<P, VEC, KS>(L);
+    for (int i = tid; i < 512; i += 512)
+        tab[i] = lfsr_next32(i < 256 ? (uint32_t)i : (uint32_t)(i - 256) << 8);
+    if (tid < np) xs[tid] = x0;
+    for (int i = tid + 512; i < np; i += 512) xs[i] = src[i];
+    __syncthreads();   // publishes the tables and the h rows
+
+    const uint16_t* xrow = (const uint16_t*)xs + (int64_t)min(r, kk - 1) * a.K;   // B column r
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_k_loop<P, VEC, 1, KS, true, true>(L, nullptr, &acc, xrow, &first);
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (tid < 8 && m0 + tid < a.M) {
+#pragma clang fp contract(off)
+        float yv = 0.f;
+        for (int s2 = 0; s2 < kk; ++s2) {
+            const int ar = 8 * (s2 & 1) + tid;          // A row of (slot s2, row m0 + tid)
+            const int dl = s2 + 16 * (ar >> 2);          // lane holding D[ar][s2]
+            const int w0 = 2 * (s2 >> 1);
+            // no contraction into an fma here: the three-launch path stores each slot
+            // output (rounded product) before the combine adds it
+            const float v = red[w0][dl][ar & 3] + red[w0 + 1][dl][ar & 3];
+            const float o = a.topk_w[s2] * v;
+            yv = s2 == 0 ? o : yv + o;
+        }
+        a.y[m0 + tid] = yv;
+    }
+}
+
 // ----------------------------------------------------------------------------------
 // Wide-token products (prefill and long token lists), vector-load layouts only
 // (K % 256 == 0, 16-byte aligned streams).  A workgroup of 16 waves owns AR = 128 weight
@@ -1217,6 +1291,20 @@ void launch_mfma(const MfmaArgs& a, bool prefill, int gridy, hipStream_t st) {
     }
 }
 
+// One token, uniform P: down and the combine in one launch (k_down_one) when the slots'
+// h rows fit its LDS budget.
+constexpr int kDownOneMaxLds = 65536;
+
+bool down_one_fits(int top_k, int K) {
+    return top_k >= 2 && top_k <= 8 && (int64_t)top_k * K * 2 <= kDownOneMaxLds;
+}
+
+template <int P>
+void launch_down_one(const MfmaArgs& b, hipStream_t st) {
+    const dim3 grid((unsigned)((b.M + 7) / 8));
+    hipLaunchKernelGGL((k_down_one<P, true>), grid, dim3(512), (size_t)b.top_k * b.K * 2, st, b);
+}
+
 // The caller's second stream and its fork / join events (seedmm_side), or all null.
 struct Side {
     hipStream_t s = nullptr;
@@ -1476,8 +1564,10 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     b.M = H; b.K = I;
     b.x = hbuf; b.ldx = I;
     b.counts = counts; b.lists = lists; b.E = E; b.T = T; b.top_k = top_k;
-    // top-1 routing: the per-slot outputs are y itself (the combine of one slot copies it)
-    const bool direct = top_k == 1;
+    // top-1 routing: the per-slot outputs are y itself (the combine of one slot copies it).
+    // One token with one P and vector layouts: down adds the slots itself (k_down_one).
+    const bool down_one = one && P != 0 && vec && down_one_fits(top_k, I);
+    const bool direct = top_k == 1 || down_one;
     b.topk_w = topk_w; b.y = direct ? y : obuf; b.ldy = H;
     b.ids = a.ids;
     b.p4mask = p4mask;
@@ -1512,7 +1602,12 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
     if (!split) {
         joined = mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st, events ? Side() : sd);
         mark(2);
-        joined = mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st, events ? Side() : sd) && joined;
+        if (down_one) {
+            if (P == 4) launch_down_one<4>(b, st);
+            else launch_down_one<3>(b, st);
+        } else {
+            joined = mfma_dispatch<MODE_DOWN>(P, vec, b, prefill, gridy, st, events ? Side() : sd) && joined;
+        }
         mark(3);
     }
     // without the join the combine could read outputs still being written: report it
