@@ -233,7 +233,9 @@ int seedmm_moe_noalloc(const int32_t *topk_ids, const float *topk_w, int T, int 
  *   events[0] before the dispatch, events[1] after it, events[2] after the gate/up
  *   kernel, events[3] after the down kernel, events[4] after the combine.  A one-token
  *   batch (T = 1) runs no dispatch kernel (its top_k ids name the experts directly), so
- *   events[0] and events[1] are recorded back to back.
+ *   events[0] and events[1] are recorded back to back; with one P, vector layouts and
+ *   2 <= top_k <= 8 it runs no combine kernel either (its down kernel adds the slots,
+ *   same bits), so events[3] and events[4] are back to back too.
  * `events` may be NULL and any entry may be NULL.  Same arguments, results and errors
  * as seedmm_moe; no event is recorded when the arguments are rejected.  When `events`
  * is not NULL every kernel runs on hip_stream (no side stream), so the recorded stage
