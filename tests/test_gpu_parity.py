@@ -363,6 +363,28 @@ def test_one_token_matches_its_batch_and_the_oracle(sm, oracle, E, H, I, P, k):
         assert rel_l2(y1[0], ref[0]) <= 1e-2, t
 
 
+@pytest.mark.parametrize("E,H,I,P,k", [
+    (10, 256, 192, 4, 2),     # two slots: one wave pair of the workgroup
+    (10, 192, 128, 4, 3),     # odd top_k: the fourth slot's lanes have no expert
+    (12, 128, 256, 3, 5),     # P = 3
+    (16, 320, 64, 4, 7),
+    (16, 64, 4160, 4, 8),     # top_k * I * 2 B above 64 KB: per-slot outputs + combine
+])
+def test_one_token_down_adds_the_slots(sm, oracle, E, H, I, P, k):
+    """One token with one P: the down kernel adds the top_k slot outputs itself in slot
+    order (when top_k * I bf16 fit its 64 KB LDS budget; beyond it the per-slot outputs
+    and the combine run).  Either way each token's bits equal those it gets inside a batch
+    (dispatch, decode kernels, combine), and the batch matches the oracle."""
+    say("one-token down with the slot sum", E, H, I, P, k)
+    gate, up, down, ids, w, x = moe_case(3, E, H, I, P, k, 6, f"d1s{k}")
+    y_b, x32 = run_moe(sm, gate, up, down, ids, w, x, E, H, I, P)
+    for t in range(3):
+        y1, _ = run_moe(sm, gate, up, down, ids[t:t + 1], w[t:t + 1], x[t:t + 1], E, H, I, P)
+        assert np.array_equal(y1[0].view(np.uint32), y_b[t].view(np.uint32)), t
+    ref = oracle.moe(ids, w, x32, E, H, I, P, gate, up, down)
+    assert rel_l2(y_b, ref) <= 1e-2
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_moe_graph_replays_match_eager(sm, T):
     """The layer call captured in a HIP graph: every replay, with eager work and
