@@ -707,7 +707,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     const uint16_t* xrow = (const uint16_t*)xs + (int64_t)min(r, kk - 1) * a.K;   // B column r
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_k_loop<P, VEC, 1, KS, true, true>(L, nullptr, &acc, xrow, &first);
+    mfma_k_loop<P, VEC, 1, KS, true, true, true>(L, nullptr, &acc, xrow, &first);
     red[wave][lane] = acc;
     __syncthreads();
     if (tid < 8 && m0 + tid < a.M) {
