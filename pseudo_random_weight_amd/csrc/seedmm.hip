@@ -1598,6 +1598,16 @@ int moe_run(const int32_t* topk_ids, const float* topk_w, int T, int top_k, cons
         mfma_dispatch<MODE_DOWN>(P, vec, pb[1], prefill, gy[1], sd.s);
         joined = sd.join_into(st);
         split = true;
+    } else if (!one && P == 0 && !events && sd.on() && sd.fork_from(st)) {
+        // mixed packs: each P's gate/up and down on a stream of its own (the P = 4 and
+        // P = 3 launches touch disjoint pairs' rows of h and of the slot outputs), with
+        // one fork and one join, so neither down launch waits for the other P's gate/up
+        mfma_dispatch<MODE_GATEUP>(4, vec, a, prefill, gridy, st);
+        mfma_dispatch<MODE_GATEUP>(3, vec, a, prefill, gridy, sd.s);
+        mfma_dispatch<MODE_DOWN>(4, vec, b, prefill, gridy, st);
+        mfma_dispatch<MODE_DOWN>(3, vec, b, prefill, gridy, sd.s);
+        joined = sd.join_into(st);
+        split = true;
     }
     if (!split) {
         joined = mfma_dispatch<MODE_GATEUP>(P, vec, a, prefill, gridy, st, events ? Side() : sd);
