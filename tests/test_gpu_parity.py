@@ -369,11 +369,12 @@ def test_one_token_matches_its_batch_and_the_oracle(sm, oracle, E, H, I, P, k):
     (12, 128, 256, 3, 5),     # P = 3
     (16, 320, 64, 4, 7),
     (16, 64, 4160, 4, 8),     # top_k * I * 2 B above 64 KB: per-slot outputs + combine
+    (16, 256, 128, 4, 12),    # top_k above 8: per-slot outputs + the general combine
 ])
 def test_one_token_down_adds_the_slots(sm, oracle, E, H, I, P, k):
     """One token with one P: the down kernel adds the top_k slot outputs itself in slot
-    order (when top_k * I bf16 fit its 64 KB LDS budget; beyond it the per-slot outputs
-    and the combine run).  Either way each token's bits equal those it gets inside a batch
+    order (for top_k <= 8 when top_k * I bf16 fit its 64 KB LDS budget; otherwise the
+    per-slot outputs and the combine run).  Either way each token's bits equal those it gets inside a batch
     (dispatch, decode kernels, combine), and the batch matches the oracle."""
     say("one-token down with the slot sum", E, H, I, P, k)
     gate, up, down, ids, w, x = moe_case(3, E, H, I, P, k, 6, f"d1s{k}")
