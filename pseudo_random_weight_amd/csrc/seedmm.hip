@@ -699,8 +699,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     L.nseg = (L.nbpr + 7) / 8;
     L.n_it = (L.nseg + KS * 4 - 1) / (KS * 4);
     const Seg<P, VEC> first = first_seg<P, VEC, KS>(L);
-    for (int i = tid; i < 512; i += 512)
-        tab[i] = lfsr_next32(i < 256 ? (uint32_t)i : (uint32_t)(i - 256) << 8);
+    tab[tid] = lfsr_next32(tid < 256 ? (uint32_t)tid : (uint32_t)(tid - 256) << 8);   // 512 threads
     if (tid < np) xs[tid] = x0;
     for (int i = tid + 512; i < np; i += 512) xs[i] = src[i];
     __syncthreads();   // publishes the tables and the h rows
@@ -733,7 +732,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 // rows (64 rows of gate and of up, or 128 rows of one matrix) for up to NC = 384 tokens,
 // so each weight block is regenerated once per pass over its expert's tokens.  It walks
 // K in 64-k steps, one barrier per step.  The waves split by role, two of each role on
-// every SIMD, so that a SIMD's vector ALU and its matrix core work at the same time:
+// every SIMD, so that each SIMD always has regeneration work and matrix work queued (on
+// gfx950 its vector ALU and matrix core measured no overlap in time, so a step costs
+// about the sum of the two; the split keeps either unit from waiting on the other's
+// latencies):
 //   - producers (waves 0-7) regenerate the next step's A tile (two blocks per lane) and
 //     stage its B tile (the step's 128-byte slice of every token row), both in LDS;
 //   - consumers (waves 8-15), wave (row half rh, token quarter tq), multiply their two
